@@ -1,0 +1,153 @@
+/*
+ * dconv1d.h - C ABI of the MI355X (gfx950) pre-norm dilated Conv1d library.
+ *
+ * Two operations, both forward only, both enqueued asynchronously on a caller stream:
+ *
+ *   1. The pre-norm residual block
+ *        out = x + Conv1d_{k=3, dilation=d, padding=d, stride=1, groups=1}(ReLU(BatchNorm1d_eval(x)))
+ *      over (N, C, L) tensors, C -> C channels, so out has the shape of x.
+ *      Source: POPCORNBENCH page "Kimi-K2.6__l2_p12" (pre-norm residual block problem),
+ *      first turn: the block definition, the per-channel eval-mode BN formula with the
+ *      running statistics, the conv's zero padding (taps t-d, t, t+d; out-of-range taps
+ *      contribute nothing) and the output-length check that gives L_out = L.
+ *
+ *   2. Conv1d(k=3, stride 1) followed by GroupNorm.
+ *      Source: POPCORNBENCH page "FW-GLM-5-1__l2_p35" (Conv1d + GroupNorm problem), its
+ *      single turn: the conv index formula t_out*stride - padding + k*dilation, GroupNorm
+ *      statistics per (sample, group) over the group's channels and all time steps with
+ *      the biased variance, the optional affine gamma/beta, and the launcher's argument
+ *      list (caller-allocated output, padding, dilation, num_groups, eps).
+ *
+ * Common rules for every compute entry point
+ *   - Pointers marked "device" are device (HBM) addresses on the current HIP device
+ *     (hipGetDevice); `stream` must belong to that device (0 = the null stream).
+ *   - N == 0 (an empty batch) is valid: nothing is launched, x and out may be NULL.
+ *   - Tensors are dense, row-major, no strides: x is [N][C][L] with L fastest, W is
+ *     PyTorch's Conv1d layout [C_out][C_in][3].
+ *   - Ownership: the caller owns and allocates every argument buffer, including out.
+ *     The library owns a per-device workspace (folded BN scale/shift, repacked weights,
+ *     GroupNorm partial statistics). It is allocated with hipMalloc on the first call
+ *     that needs more than the current size (hipFree of the old one synchronises the
+ *     device), kept for later calls, and freed by dconv1d_release().
+ *   - All calls on one device share that workspace: calls that may overlap in time
+ *     on different streams of the same device race. Serialise them on one stream.
+ *   - No host synchronisation and no device-to-host reads happen on a call once the
+ *     workspace is large enough; the call returns as soon as its kernels are queued.
+ *   - Argument validation happens on the host before any HIP call; a rejected call
+ *     touches no device state.
+ *   - Return value: DCONV1D_OK (0) or a negative DCONV1D_E* code. dconv1d_last_error()
+ *     then returns a message for the calling thread. Nothing aborts or throws across
+ *     the ABI.
+ */
+#ifndef DCONV1D_H
+#define DCONV1D_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DCONV1D_OK 0
+/* A required pointer is NULL, a size is out of range (N < 0, C < 1, L < 1, d < 1,
+ * C_out % num_groups != 0, T_out < 1, eps < 0 or NaN), or an index would not fit the
+ * library's 32-bit per-sample indexing (C*L >= 2^31). */
+#define DCONV1D_EINVAL -1
+/* `out` overlaps `x`. The kernels read x taps belonging to neighbouring output tiles
+ * while other tiles are already writing out, so in-place operation is not supported. */
+#define DCONV1D_EALIAS -2
+/* A HIP runtime call or kernel launch failed (the message names the HIP error). */
+#define DCONV1D_EHIP -3
+/* The workspace could not be allocated. */
+#define DCONV1D_ENOMEM -4
+
+/*
+ * prenorm_dconv1d_fwd - the pre-norm residual block in float32.
+ *
+ *   x            device, float32 [N][C][L]          input, also the residual
+ *   running_mean device, float32 [C]                BN running mean
+ *   running_var  device, float32 [C]                BN running variance
+ *   gamma, beta  device, float32 [C]                BN affine weight and bias
+ *   eps          BN epsilon, added to the variance inside the square root
+ *   W            device, float32 [C][C][3]          conv weight, PyTorch layout
+ *   b            device, float32 [C] or NULL        conv bias (NULL means zero)
+ *   out          device, float32 [N][C][L]          result; must not overlap x
+ *   N, C, L      batch, channels, length (N == 0 is a no-op that returns DCONV1D_OK)
+ *   d            dilation; padding is d and the kernel size is 3 (any d >= 1; d >= L
+ *                leaves only the centre tap)
+ *   stream       HIP stream the work is queued on
+ *
+ * BN is the eval-mode form: scale = gamma/sqrt(var+eps), shift = beta - mean*scale,
+ * folded once per call in double precision and rounded to float. The conv input is
+ * zero-padded after the ReLU, so padded taps contribute exactly 0. Arithmetic:
+ * float32 products, float32 accumulation (MFMA), bias and residual added in float32.
+ */
+int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* running_var,
+                        const float* gamma, const float* beta, float eps,
+                        const float* W, const float* b, float* out,
+                        int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream);
+
+/*
+ * prenorm_dconv1d_fwd_bf16 - the same block with bfloat16 storage of x and out.
+ *
+ * x and out are bfloat16 bit patterns (uint16_t, [N][C][L]); every other argument is
+ * as in prenorm_dconv1d_fwd (float32 parameters, W in float32 PyTorch layout). BN and
+ * ReLU run in float32 on the bfloat16 x, the activation and W are rounded to bfloat16
+ * (round to nearest even) for the bf16 MFMA, products accumulate in float32, bias and
+ * the bfloat16 residual are added in float32, and out is rounded to bfloat16 (RNE).
+ */
+int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
+                             const float* running_var, const float* gamma, const float* beta,
+                             float eps, const float* W, const float* b, uint16_t* out,
+                             int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream);
+
+/*
+ * conv1d_groupnorm_fwd - GroupNorm(Conv1d_{k=3, stride 1}(x)) in float32.
+ *
+ *   x            device, float32 [N][C_in][T]
+ *   W            device, float32 [C_out][C_in][3]      conv weight, PyTorch layout
+ *   bias         device, float32 [C_out] or NULL       conv bias (NULL means none)
+ *   gamma, beta  device, float32 [C_out] or NULL       GroupNorm affine parameters; NULL
+ *                                                      gamma means 1, NULL beta means 0
+ *   eps          added to the biased group variance inside the square root
+ *   num_groups   G; groups are contiguous blocks of C_out/G channels
+ *   out          device, float32 [N][C_out][T_out], T_out = T + 2*padding - 2*dilation;
+ *                must not overlap x
+ *   padding >= 0, dilation >= 1; T_out must be >= 1
+ *
+ * The conv stores its result into out while writing per-(sample, channel, time tile)
+ * partial sums and centred sums of squares to the workspace; a second kernel merges
+ * them per (sample, group) in a fixed order in double precision and normalises out in
+ * place. Results are bitwise reproducible from run to run.
+ */
+int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias,
+                         const float* gamma, const float* beta, float eps,
+                         int64_t num_groups, float* out,
+                         int64_t N, int64_t C_in, int64_t C_out, int64_t T,
+                         int64_t padding, int64_t dilation, hipStream_t stream);
+
+/* Message describing the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next library call on the same thread. */
+const char* dconv1d_last_error(void);
+
+/* Frees the workspace of every device. Waits for the device first (hipFree does).
+ * Safe to call at any time when no library call is in flight; later calls reallocate. */
+void dconv1d_release(void);
+
+/*
+ * Kernel timing for measurement tools. While enabled, each compute call records a
+ * pair of HIP events on its stream around its dominant kernel (the fused conv kernel).
+ * dconv1d_timer_read waits for the last recorded event, returns the summed duration
+ * in milliseconds and the number of timed launches through the out-pointers, and
+ * clears the record. At most 4096 launches are recorded between reads; later ones
+ * are not timed. Returns DCONV1D_OK or DCONV1D_EHIP.
+ */
+int dconv1d_timer_enable(int enable);
+int dconv1d_timer_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCONV1D_H */

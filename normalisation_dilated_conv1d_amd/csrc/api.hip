@@ -1,0 +1,366 @@
+// C ABI of the library (declared in include/dconv1d.h): argument validation, the
+// per-device workspace, kernel launches and the optional kernel timer.
+//
+// Validation follows the checks of the pages' host wrappers (POPCORNBENCH
+// "Kimi-K2.6__l2_p12", first turn: device/contiguity checks, kernel size 3 with
+// padding = dilation so the output keeps length L, 32-bit index limits; and
+// "FW-GLM-5-1__l2_p35": output length T + 2p - d(k-1), channels divisible by groups),
+// restated as status codes instead of exceptions.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dconv1d.h"
+#include "internal.h"
+
+using namespace dconv1d;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DCONV1D_EHIP, "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return abytes > 0 && bbytes > 0 && a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// ---------------------------------------------------------------- per-device workspace
+constexpr int kMaxDevices = 64;
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+Workspace g_ws[kMaxDevices];
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int get_workspace(size_t bytes, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DCONV1D_EINVAL, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[dev];
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      // earlier calls may still be using the old buffer
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t sz = (bytes + (size_t(2) << 20) - 1) & ~((size_t(2) << 20) - 1);
+    e = hipMalloc(&w.ptr, sz);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      w.ptr = nullptr;
+      return fail(DCONV1D_ENOMEM, "workspace hipMalloc of %zu bytes failed: %s", sz,
+                  hipGetErrorString(e));
+    }
+    w.bytes = sz;
+  }
+  *out = static_cast<char*>(w.ptr);
+  return DCONV1D_OK;
+}
+
+// ---------------------------------------------------------------- kernel timer
+constexpr int kTimerSlots = 4096;
+struct Timer {
+  bool on = false;
+  int device = -1;
+  std::vector<hipEvent_t> ev;  // 2 per slot
+  int used = 0;
+};
+std::mutex g_timer_mu;
+Timer g_timer;
+
+int timer_begin(hipStream_t s) {
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  if (!g_timer.on || g_timer.used >= kTimerSlots) return -1;
+  const int slot = g_timer.used++;
+  if (hipEventRecord(g_timer.ev[2 * slot], s) != hipSuccess) return -1;
+  return slot;
+}
+void timer_end(int slot, hipStream_t s) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  (void)hipEventRecord(g_timer.ev[2 * slot + 1], s);
+}
+
+// ---------------------------------------------------------------- shared checks
+constexpr int64_t kMaxChannels = 16384;
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+
+int check_sizes_block(int64_t N, int64_t C, int64_t L, int64_t d, float eps) {
+  if (N < 0) return fail(DCONV1D_EINVAL, "N must be >= 0 (got %lld)", (long long)N);
+  if (C < 1 || C > kMaxChannels)
+    return fail(DCONV1D_EINVAL, "C must be in [1, %lld] (got %lld)", (long long)kMaxChannels,
+                (long long)C);
+  if (L < 1 || L >= (int64_t(1) << 30))
+    return fail(DCONV1D_EINVAL, "L must be in [1, 2^30) (got %lld)", (long long)L);
+  if (d < 1) return fail(DCONV1D_EINVAL, "dilation d must be >= 1 (got %lld)", (long long)d);
+  if (!(eps >= 0.f) || std::isinf(eps))
+    return fail(DCONV1D_EINVAL, "eps must be finite and >= 0");
+  if (C * L > kMaxIndex)
+    return fail(DCONV1D_EINVAL, "C*L = %lld exceeds 2^31-1", (long long)(C * L));
+  return DCONV1D_OK;
+}
+
+template <typename XT>
+int prenorm_common(const XT* x, const float* running_mean, const float* running_var,
+                   const float* gamma, const float* beta, float eps, const float* W,
+                   const float* b, XT* out, int64_t N, int64_t C, int64_t L, int64_t d,
+                   hipStream_t stream, bool bf16) {
+  // an empty batch has no data: x and out may then be NULL (torch gives empty tensors
+  // a null data pointer)
+  if (!x && N != 0) return fail(DCONV1D_EINVAL, "x is NULL");
+  if (!running_mean) return fail(DCONV1D_EINVAL, "running_mean is NULL");
+  if (!running_var) return fail(DCONV1D_EINVAL, "running_var is NULL");
+  if (!gamma) return fail(DCONV1D_EINVAL, "gamma is NULL");
+  if (!beta) return fail(DCONV1D_EINVAL, "beta is NULL");
+  if (!W) return fail(DCONV1D_EINVAL, "W is NULL");
+  if (!out && N != 0) return fail(DCONV1D_EINVAL, "out is NULL");
+  int st = check_sizes_block(N, C, L, d, eps);
+  if (st != DCONV1D_OK) return st;
+  const int64_t per_sample = C * L;
+  if (N > INT64_MAX / (per_sample * (int64_t)sizeof(XT)))
+    return fail(DCONV1D_EINVAL, "N*C*L overflows");
+  const uint64_t bytes = (uint64_t)N * per_sample * sizeof(XT);
+  if (overlaps(x, bytes, out, bytes)) return fail(DCONV1D_EALIAS, "out overlaps x");
+
+  const int Ci = (int)C, Li = (int)L;
+  const int Cin_pad = round_up(Ci, KC);
+  const int Cout_pad = round_up(Ci, CO_TILE_F32);
+  const int n_ct = Cout_pad / CO_TILE_F32;
+  const int tile_t = conv_f32_tile_t(EPI_RESIDUAL, Li, (int)std::min<int64_t>(N * n_ct, kMaxIndex));
+  const int n_tt = (Li + tile_t - 1) / tile_t;
+  if (N * n_tt * n_ct > kMaxIndex)
+    return fail(DCONV1D_EINVAL, "grid of %lld workgroups is too large",
+                (long long)(N * n_tt * n_ct));
+  if (N == 0) return DCONV1D_OK;
+
+  // d >= L: both outer taps are always in the padding; d = L gives the same result and
+  // keeps every tap offset inside int range.
+  const int d_eff = (int)std::min<int64_t>(d, L);
+
+  const size_t off_scale = 0;
+  const size_t off_shift = align256(off_scale + sizeof(float) * Cin_pad);
+  const size_t off_wp = align256(off_shift + sizeof(float) * Cin_pad);
+  const size_t total = align256(off_wp + sizeof(float) * 3 * (size_t)Cin_pad * Cout_pad);
+  char* ws = nullptr;
+  st = get_workspace(total, &ws);
+  if (st != DCONV1D_OK) return st;
+  float* scale = reinterpret_cast<float*>(ws + off_scale);
+  float* shift = reinterpret_cast<float*>(ws + off_shift);
+  float* Wp = reinterpret_cast<float*>(ws + off_wp);
+
+  hipError_t e = launch_prep_f32(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var,
+                                 gamma, beta, eps, scale, shift, stream);
+  if (e != hipSuccess) return hip_fail(e, "prep kernel launch");
+
+  ConvF32Args a{};
+  a.x = x;
+  a.scale = scale;
+  a.shift = shift;
+  a.Wp = Wp;
+  a.bias = b;
+  a.out = out;
+  a.partials = nullptr;
+  a.N = (int)N;
+  a.C_in = Ci;
+  a.C_out = Ci;
+  a.L_in = Li;
+  a.L_out = Li;
+  a.pad = d_eff;
+  a.dil = d_eff;
+  a.NCB = Cout_pad / 32;
+  a.Q = 3 * Cin_pad / KC;
+  a.n_tt = n_tt;
+  a.n_ct = n_ct;
+  const int slot = timer_begin(stream);
+  e = launch_conv_f32(a, tile_t, EPI_RESIDUAL, bf16, stream);
+  timer_end(slot, stream);
+  if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
+  return DCONV1D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* running_var,
+                        const float* gamma, const float* beta, float eps, const float* W,
+                        const float* b, float* out, int64_t N, int64_t C, int64_t L, int64_t d,
+                        hipStream_t stream) {
+  g_err.clear();
+  return prenorm_common<float>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N, C,
+                               L, d, stream, false);
+}
+
+int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
+                             const float* running_var, const float* gamma, const float* beta,
+                             float eps, const float* W, const float* b, uint16_t* out,
+                             int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream) {
+  g_err.clear();
+  return prenorm_common<uint16_t>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
+                                  C, L, d, stream, true);
+}
+
+int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, const float* gamma,
+                         const float* beta, float eps, int64_t num_groups, float* out, int64_t N,
+                         int64_t C_in, int64_t C_out, int64_t T, int64_t padding,
+                         int64_t dilation, hipStream_t stream) {
+  g_err.clear();
+  if (!x && N != 0) return fail(DCONV1D_EINVAL, "x is NULL");
+  if (!W) return fail(DCONV1D_EINVAL, "W is NULL");
+  if (!out && N != 0) return fail(DCONV1D_EINVAL, "out is NULL");
+  if (N < 0) return fail(DCONV1D_EINVAL, "N must be >= 0 (got %lld)", (long long)N);
+  if (C_in < 1 || C_in > kMaxChannels || C_out < 1 || C_out > kMaxChannels)
+    return fail(DCONV1D_EINVAL, "C_in and C_out must be in [1, %lld]", (long long)kMaxChannels);
+  if (num_groups < 1 || C_out % num_groups != 0)
+    return fail(DCONV1D_EINVAL, "num_groups must be >= 1 and divide C_out (got %lld, C_out %lld)",
+                (long long)num_groups, (long long)C_out);
+  if (T < 1 || T >= (int64_t(1) << 29))
+    return fail(DCONV1D_EINVAL, "T must be in [1, 2^29) (got %lld)", (long long)T);
+  if (padding < 0 || padding >= (int64_t(1) << 29))
+    return fail(DCONV1D_EINVAL, "padding must be in [0, 2^29)");
+  if (dilation < 1) return fail(DCONV1D_EINVAL, "dilation must be >= 1");
+  const int64_t T_out = T + 2 * padding - 2 * dilation;
+  if (T_out < 1)
+    return fail(DCONV1D_EINVAL, "output length T + 2*padding - 2*dilation = %lld < 1",
+                (long long)T_out);
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(DCONV1D_EINVAL, "eps must be finite and >= 0");
+  if (C_in * T > kMaxIndex || C_out * T_out > kMaxIndex)
+    return fail(DCONV1D_EINVAL, "C*T exceeds 2^31-1");
+  if (N > INT64_MAX / (4 * std::max(C_in * T, C_out * T_out)))
+    return fail(DCONV1D_EINVAL, "N*C*T overflows");
+  if (overlaps(x, (uint64_t)N * C_in * T * 4, out, (uint64_t)N * C_out * T_out * 4))
+    return fail(DCONV1D_EALIAS, "out overlaps x");
+
+  const int Cin_pad = round_up((int)C_in, KC);
+  const int Cout_pad = round_up((int)C_out, CO_TILE_F32);
+  const int n_ct = Cout_pad / CO_TILE_F32;
+  const int Lo = (int)T_out;
+  const int tile_t = conv_f32_tile_t(EPI_GN_STATS, Lo, (int)std::min<int64_t>(N * n_ct, kMaxIndex));
+  const int n_tt = (Lo + tile_t - 1) / tile_t;
+  if (N * n_tt * n_ct > kMaxIndex) return fail(DCONV1D_EINVAL, "grid too large");
+  if (N == 0) return DCONV1D_OK;
+
+  const size_t off_wp = 0;
+  const size_t off_part = align256(off_wp + sizeof(float) * 3 * (size_t)Cin_pad * Cout_pad);
+  const size_t total = align256(off_part + sizeof(float) * 2 * (size_t)N * C_out * n_tt);
+  char* ws = nullptr;
+  int st = get_workspace(total, &ws);
+  if (st != DCONV1D_OK) return st;
+  float* Wp = reinterpret_cast<float*>(ws + off_wp);
+  float* part = reinterpret_cast<float*>(ws + off_part);
+
+  hipError_t e = launch_prep_f32(W, (int)C_out, (int)C_in, Cout_pad, Cin_pad, Wp, nullptr,
+                                 nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e, "prep kernel launch");
+
+  // dilation > T + 2*padding would already make T_out < 1, so taps fit in int
+  ConvF32Args a{};
+  a.x = x;
+  a.scale = nullptr;
+  a.shift = nullptr;
+  a.Wp = Wp;
+  a.bias = bias;
+  a.out = out;
+  a.partials = part;
+  a.N = (int)N;
+  a.C_in = (int)C_in;
+  a.C_out = (int)C_out;
+  a.L_in = (int)T;
+  a.L_out = Lo;
+  a.pad = (int)padding;
+  a.dil = (int)dilation;
+  a.NCB = Cout_pad / 32;
+  a.Q = 3 * Cin_pad / KC;
+  a.n_tt = n_tt;
+  a.n_ct = n_ct;
+  const int slot = timer_begin(stream);
+  e = launch_conv_f32(a, tile_t, EPI_GN_STATS, false, stream);
+  timer_end(slot, stream);
+  if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
+  e = launch_gn_normalize(out, part, gamma, beta, eps, (int)N, (int)C_out, Lo, (int)num_groups,
+                          n_tt, tile_t, stream);
+  if (e != hipSuccess) return hip_fail(e, "groupnorm kernel launch");
+  return DCONV1D_OK;
+}
+
+const char* dconv1d_last_error(void) { return g_err.c_str(); }
+
+void dconv1d_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    if (!g_ws[dev].ptr) continue;
+    if (hipSetDevice(dev) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(g_ws[dev].ptr);
+    }
+    g_ws[dev].ptr = nullptr;
+    g_ws[dev].bytes = 0;
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+}
+
+int dconv1d_timer_enable(int enable) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  if (enable && g_timer.ev.empty()) {
+    g_timer.ev.resize(2 * kTimerSlots);
+    for (auto& ev : g_timer.ev) {
+      hipError_t e = hipEventCreate(&ev);
+      if (e != hipSuccess) {
+        g_timer.ev.clear();
+        return hip_fail(e, "hipEventCreate");
+      }
+    }
+  }
+  g_timer.on = enable != 0;
+  g_timer.used = 0;
+  return DCONV1D_OK;
+}
+
+int dconv1d_timer_read(double* total_ms, int64_t* launches) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  double sum = 0.0;
+  for (int i = 0; i < g_timer.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = g_timer.used;
+  g_timer.used = 0;
+  return DCONV1D_OK;
+}
+
+}  // extern "C"

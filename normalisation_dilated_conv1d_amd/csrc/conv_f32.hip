@@ -1,0 +1,295 @@
+// Float32 implicit-GEMM kernel for a kernel-3, stride-1 Conv1d on MI355X (gfx950).
+//
+// It serves both operations of the library:
+//   * the pre-norm residual block (POPCORNBENCH "Kimi-K2.6__l2_p12", first turn): each
+//     conv input value is ReLU(BN_eval(x)) applied while the tile is staged, padded taps
+//     are exact zeros, and the epilogue adds the conv bias and the raw x residual;
+//   * Conv1d + GroupNorm (POPCORNBENCH "FW-GLM-5-1__l2_p35"): the staged value is x
+//     itself, and the epilogue stores the conv output together with per-channel tile
+//     statistics for the GroupNorm pass.
+//
+// GEMM view (the three-tap decomposition of the first page's design turn): for one
+// sample, out[co][t] = sum over K = (tap k, input channel ci) of
+// W[co][ci][k] * z[ci][t - pad + k*dil], i.e. M = C_out, N = time, K = 3*C_in.
+//
+// Work split
+//   workgroup  = one sample n, 256 output channels (co tile), TT time steps (t tile);
+//                4 waves, wave w owns output channels [64w, 64w+64) of the co tile and
+//                all TT time steps: 2 x (TT/32) MFMA 32x32 accumulator blocks.
+//   K loop     = chunks of 32 input channels of one tap, ordered (ci-block, tap) so
+//                that the three taps of a channel block are staged back to back and hit
+//                the same L2 lines.
+//   B operand  = the activation tile z[32][TT], staged through LDS once per chunk by
+//                all 256 threads (global loads coalesced along t, BN+ReLU applied in
+//                registers, zero outside [0, L_in)), double-buffered, one barrier per
+//                chunk.
+//   A operand  = the weights, read straight from global memory into registers: the
+//                repack kernel stores them in the exact lane order of the MFMA A operand,
+//                so each lane fetches 4 consecutive K values with one 16-byte load and
+//                each wave reads 1 KB contiguous per load. No LDS for W: no two waves of
+//                a workgroup use the same weights.
+//   MFMA       = v_mfma_f32_32x32x2_f32 (full float32 products and accumulation).
+//
+// K permutation inside a chunk: the 32 rows r of a chunk are split as r = 8g + 4h + u
+// (g: 4 groups, h: the lane's half-wave, u: 4 steps). MFMA step (g, u) uses rows
+// 8g + u (lanes 0-31) and 8g + 4 + u (lanes 32-63) as its two K values, so a lane's
+// four A values for steps u = 0..3 are contiguous in the repacked weights. A and B use
+// the same permutation, so the sum over K is unchanged.
+//
+// Workgroup order is XCD-aware: the hardware sends workgroup b to XCD b % 8, so the
+// logical tile index is remapped to give every XCD one contiguous range of tiles; the
+// neighbouring time tiles whose tap windows overlap then share that XCD's L2.
+
+#include "internal.h"
+
+namespace dconv1d {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Sum over the 32 lanes of each half-wave with ds_swizzle butterflies (xor 16..1).
+// Every lane ends with the same, order-fixed value.
+template <int XOR>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (XOR << 10) | 0x1F));
+}
+__device__ __forceinline__ float halfwave_sum(float v) {
+  v += swz_xor<16>(v);
+  v += swz_xor<8>(v);
+  v += swz_xor<4>(v);
+  v += swz_xor<2>(v);
+  v += swz_xor<1>(v);
+  return v;
+}
+
+// Storage conversions. bfloat16 is carried as its 16-bit pattern; widening is exact,
+// narrowing rounds to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ void from_f32(float v, float* dst) { *dst = v; }
+__device__ __forceinline__ void from_f32(float v, uint16_t* dst) {
+  const uint32_t u = __float_as_uint(v);
+  uint16_t r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) r = (uint16_t)((u >> 16) | 0x40u);
+  else r = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  *dst = r;
+}
+
+template <int TT, bool BN, int EPI, typename XT>
+__global__ void __launch_bounds__(NTHREADS)
+conv_f32_kernel(ConvF32Args a) {
+  constexpr int NJ = TT / 32;                    // 32-column MFMA blocks per wave
+  constexpr int XPT = KC * TT / NTHREADS;        // staged values per thread per chunk
+  constexpr int RPP = NTHREADS / TT;             // rows covered by one pass of the workgroup
+  constexpr int PITCH = TT + 8;                  // LDS row pitch (floats); +8 staggers the
+                                                 // two half-wave rows onto different banks
+  __shared__ float zs[2][KC * PITCH];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int h = l >> 5;
+  const int lc = l & 31;
+
+  // XCD-aware tile order.
+  const int nwg = gridDim.x;
+  const int b = blockIdx.x;
+  const int per = nwg >> 3, rem = nwg & 7, xcd = b & 7;
+  const int logical = xcd * per + min(xcd, rem) + (b >> 3);
+  const int ct = logical % a.n_ct;
+  const int rest = logical / a.n_ct;
+  const int tt = rest % a.n_tt;
+  const int n = rest / a.n_tt;
+  const int t0 = tt * TT;
+
+  const XT* __restrict__ xn = reinterpret_cast<const XT*>(a.x) + (size_t)n * a.C_in * a.L_in;
+
+  // Staging map: thread covers column `col` of rows r0, r0 + RPP, ... (r0 is wave-uniform).
+  const int col = tid % TT;
+  const int r0 = __builtin_amdgcn_readfirstlane(tid / TT);
+
+  const f32x4* __restrict__ Wp4 = reinterpret_cast<const f32x4*>(a.Wp);
+  const int cb0 = (ct * CO_TILE_F32) / 32 + 2 * w;
+
+  f32x16 acc[2][NJ];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nj][r] = 0.f;
+
+  float xr[XPT];
+  f32x4 wc[4][2], wn[4][2];
+
+  auto load_x = [&](int q) {
+    const int c = q / 3, k = q - 3 * c;
+    const int ts = t0 + col + k * a.dil - a.pad;
+    const bool tok = ts >= 0 && ts < a.L_in;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int ci = c * KC + r0 + RPP * i;
+      xr[i] = (tok && ci < a.C_in) ? to_f32(xn[ci * a.L_in + ts]) : 0.f;
+    }
+  };
+  auto store_z = [&](int q, float* dst) {
+    const int c = q / 3, k = q - 3 * c;
+    const int ts = t0 + col + k * a.dil - a.pad;
+    const bool tok = ts >= 0 && ts < a.L_in;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int row = r0 + RPP * i;
+      const int ci = c * KC + row;
+      float v = xr[i];
+      if (BN) {
+        // z = ReLU(scale*x + shift) inside the input, exactly 0 in the padding.
+        v = (tok && ci < a.C_in) ? fmaxf(fmaf(v, a.scale[ci], a.shift[ci]), 0.f) : 0.f;
+      }
+      dst[row * PITCH + col] = v;
+    }
+  };
+  auto load_w = [&](int q, f32x4 (&dst)[4][2]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        dst[g][mb] = Wp4[((q * 4 + g) * a.NCB + cb0 + mb) * 64 + l];
+  };
+
+  load_x(0);
+  load_w(0, wc);
+  store_z(0, zs[0]);
+  __syncthreads();
+
+  for (int q = 0; q < a.Q; ++q) {
+    const bool more = q + 1 < a.Q;
+    if (more) {
+      load_x(q + 1);
+      load_w(q + 1, wn);
+    }
+    const float* zb = zs[q & 1];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = 8 * g + 4 * h + u;
+        float bv[NJ];
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) bv[nj] = zb[row * PITCH + 32 * nj + lc];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const float av = wc[g][mb][u];
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj)
+            acc[mb][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv[nj], acc[mb][nj], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+      store_z(q + 1, zs[(q + 1) & 1]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) wc[g][mb] = wn[g][mb];
+    }
+    __syncthreads();
+  }
+
+  // Epilogue. Accumulator register r of block (mb, nj) holds output channel
+  // 32*mb + 8*(r/4) + 4*h + r%4 (within the wave's 64) and time 32*nj + lc.
+  XT* __restrict__ outn = reinterpret_cast<XT*>(a.out) + (size_t)n * a.C_out * a.L_out;
+  const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * h;
+  if (EPI == EPI_RESIDUAL) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int co = co_base + 32 * mb + 8 * (r >> 2) + (r & 3);
+        if (co < a.C_out) {
+          const float bco = a.bias ? a.bias[co] : 0.f;
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj) {
+            const int t = t0 + 32 * nj + lc;
+            if (t < a.L_out) {
+              // residual: C_in == C_out and L_in == L_out for the block
+              from_f32(acc[mb][nj][r] + bco + to_f32(xn[co * a.L_in + t]), &outn[co * a.L_out + t]);
+            }
+          }
+        }
+      }
+  } else {
+    const int cnt = min(TT, a.L_out - t0);
+    const float inv_cnt = 1.f / (float)cnt;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int co = co_base + 32 * mb + 8 * (r >> 2) + (r & 3);
+        const bool cok = co < a.C_out;
+        const float bco = (cok && a.bias) ? a.bias[co] : 0.f;
+        float y[NJ];
+        float s = 0.f;
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) {
+          y[nj] = acc[mb][nj][r] + bco;
+          s += (t0 + 32 * nj + lc < a.L_out) ? y[nj] : 0.f;
+        }
+        s = halfwave_sum(s);
+        const float mean = s * inv_cnt;
+        float m2 = 0.f;
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) {
+          const float dv = y[nj] - mean;
+          m2 += (t0 + 32 * nj + lc < a.L_out) ? dv * dv : 0.f;
+        }
+        m2 = halfwave_sum(m2);
+        if (cok) {
+          if (lc == 0) {
+            float* p = a.partials + (((size_t)n * a.C_out + co) * a.n_tt + tt) * 2;
+            p[0] = s;
+            p[1] = m2;
+          }
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj) {
+            const int t = t0 + 32 * nj + lc;
+            if (t < a.L_out) from_f32(y[nj], &outn[co * a.L_out + t]);
+          }
+        }
+      }
+  }
+}
+
+// Time-tile width: 128 normally; 64 when 128 would leave the GPU's 256 CUs short of
+// workgroups (small batch x length, as in the GroupNorm workload).
+int conv_f32_tile_t(int epilogue, int L_out, int tiles_other) {
+  (void)epilogue;
+  const long long wg128 = (long long)tiles_other * ((L_out + 127) / 128);
+  return wg128 >= 512 ? 128 : 64;
+}
+
+template <int TT, bool BN, int EPI, typename XT>
+static hipError_t launch_one(const ConvF32Args& a, int nwg, hipStream_t stream) {
+  hipLaunchKernelGGL((conv_f32_kernel<TT, BN, EPI, XT>), dim3(nwg), dim3(NTHREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, bool bf16_storage,
+                           hipStream_t stream) {
+  const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const bool bn = a.scale != nullptr;
+  if (epilogue == EPI_RESIDUAL) {
+    if (!bn) return hipErrorInvalidValue;
+    if (bf16_storage)
+      return tile_t == 128 ? launch_one<128, true, EPI_RESIDUAL, uint16_t>(a, (int)nwg, stream)
+                           : launch_one<64, true, EPI_RESIDUAL, uint16_t>(a, (int)nwg, stream);
+    return tile_t == 128 ? launch_one<128, true, EPI_RESIDUAL, float>(a, (int)nwg, stream)
+                         : launch_one<64, true, EPI_RESIDUAL, float>(a, (int)nwg, stream);
+  }
+  if (bn || bf16_storage) return hipErrorInvalidValue;
+  return tile_t == 128 ? launch_one<128, false, EPI_GN_STATS, float>(a, (int)nwg, stream)
+                       : launch_one<64, false, EPI_GN_STATS, float>(a, (int)nwg, stream);
+}
+
+}  // namespace dconv1d

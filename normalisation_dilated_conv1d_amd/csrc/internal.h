@@ -1,0 +1,52 @@
+// Internal declarations shared by the library's HIP translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace dconv1d {
+
+// K-chunk: 32 input channels of one tap. One chunk is one LDS stage.
+constexpr int KC = 32;
+// Output channels per workgroup in the float32 kernel: 4 waves x 64 channels.
+constexpr int CO_TILE_F32 = 256;
+constexpr int NTHREADS = 256;
+
+// Arguments of the float32 implicit-GEMM conv kernel. Sizes are int: the host checks
+// that every per-sample index (C*L) fits in 31 bits; the sample offset is 64-bit.
+struct ConvF32Args {
+  const void* x;         // [N][C_in][L_in], float32 or bfloat16 bits
+  const float* scale;    // [Cin_pad] folded BN scale (nullptr: no BN/ReLU on load)
+  const float* shift;    // [Cin_pad] folded BN shift
+  const float* Wp;       // repacked weights, see prep.hip
+  const float* bias;     // [C_out] or nullptr
+  void* out;             // [N][C_out][L_out], same storage type as x
+  float* partials;       // GroupNorm: [N][C_out][n_tt][2] (tile sum, centred sum of squares)
+  int N, C_in, C_out, L_in, L_out;
+  int pad, dil;          // tap k reads input t - pad + k*dil
+  int NCB;               // 32-channel output blocks in the repacked weights (Cout_pad/32)
+  int Q;                 // number of K-chunks = 3 * Cin_pad / KC
+  int n_tt, n_ct;        // time tiles, output-channel tiles
+};
+
+enum ConvEpilogue { EPI_RESIDUAL = 0, EPI_GN_STATS = 1 };
+
+inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+// prep.hip
+hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, int Cin_pad,
+                           float* Wp, const float* running_mean, const float* running_var,
+                           const float* gamma, const float* beta, float eps, float* scale,
+                           float* shift, hipStream_t stream);
+
+// conv_f32.hip
+int conv_f32_tile_t(int epilogue, int L_out, int tiles_other);
+hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, bool bf16_storage,
+                           hipStream_t stream);
+
+// gn.hip
+hipError_t launch_gn_normalize(float* out, const float* partials, const float* gamma,
+                               const float* beta, float eps, int N, int C_out, int L_out,
+                               int num_groups, int n_tt, int tile_t, hipStream_t stream);
+
+}  // namespace dconv1d

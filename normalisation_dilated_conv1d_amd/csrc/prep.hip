@@ -1,0 +1,80 @@
+// Per-call preparation for the float32 conv kernel, in one launch:
+//
+// 1. BN fold (POPCORNBENCH "Kimi-K2.6__l2_p12", first turn: eval-mode BN per channel,
+//    with the inverse standard deviation precomputed once per channel as on that page):
+//      scale[c] = gamma[c] / sqrt(running_var[c] + eps)
+//      shift[c] = beta[c] - running_mean[c] * scale[c]
+//    computed in double and rounded once to float, so the staged activation is
+//    ReLU(fma(x, scale, shift)). Channels in [C_in, Cin_pad) get scale = shift = 0.
+//
+// 2. Weight repack from PyTorch's [C_out][C_in][3] into the register order of the MFMA
+//    A operand (the first page's design turn proposes a transposed weight layout so the
+//    output-channel loop is contiguous; this goes one step further, to lane order).
+//    Index, in 16-byte units:   ((q*4 + g)*NCB + cb)*64 + lane
+//      q    = 3*c + k     K-chunk: input-channel block c (32 channels), tap k
+//      g    = 0..3        group of 8 rows inside the chunk
+//      cb   = 0..NCB-1    block of 32 output channels
+//      lane = 0..63       co = 32*cb + lane%32, rows 8g + 4*(lane/32) + u, u = 0..3
+//    and the 4 floats of the unit are u = 0..3:
+//      Wp[unit][u] = W[co][32c + 8g + 4*(lane/32) + u][k]   (0 outside C_out x C_in).
+//    A wave of the conv kernel then loads 1 KB contiguous per (q, g, cb) and each lane
+//    holds its A values for four consecutive MFMA steps.
+
+#include "internal.h"
+
+namespace dconv1d {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256)
+prep_f32_kernel(const float* __restrict__ W, int C_out, int C_in, int NCB, int total4,
+                f32x4* __restrict__ Wp, const float* __restrict__ mean,
+                const float* __restrict__ var, const float* __restrict__ gamma,
+                const float* __restrict__ beta, float eps, float* __restrict__ scale,
+                float* __restrict__ shift, int Cin_pad) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < total4) {
+    const int lane = idx & 63;
+    int rest = idx >> 6;
+    const int cb = rest % NCB;
+    rest /= NCB;
+    const int g = rest & 3;
+    const int q = rest >> 2;
+    const int c = q / 3, k = q - 3 * c;
+    const int co = 32 * cb + (lane & 31);
+    const int ci0 = 32 * c + 8 * g + 4 * (lane >> 5);
+    f32x4 v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ci = ci0 + u;
+      v[u] = (co < C_out && ci < C_in) ? W[((size_t)co * C_in + ci) * 3 + k] : 0.f;
+    }
+    Wp[idx] = v;
+  }
+  if (scale != nullptr && idx < Cin_pad) {
+    float sc = 0.f, sh = 0.f;
+    if (idx < C_in) {
+      const double s = (double)gamma[idx] / sqrt((double)var[idx] + (double)eps);
+      sc = (float)s;
+      sh = (float)((double)beta[idx] - (double)mean[idx] * s);
+    }
+    scale[idx] = sc;
+    shift[idx] = sh;
+  }
+}
+
+hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, int Cin_pad,
+                           float* Wp, const float* running_mean, const float* running_var,
+                           const float* gamma, const float* beta, float eps, float* scale,
+                           float* shift, hipStream_t stream) {
+  const int NCB = Cout_pad / 32;
+  const long long total4 = 3LL * Cin_pad * Cout_pad / 4;
+  const long long threads = total4 > Cin_pad ? total4 : Cin_pad;
+  const int blocks = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL(prep_f32_kernel, dim3(blocks), dim3(256), 0, stream, W, C_out, C_in, NCB,
+                     (int)total4, reinterpret_cast<f32x4*>(Wp), running_mean, running_var,
+                     gamma, beta, eps, scale, shift, Cin_pad);
+  return hipGetLastError();
+}
+
+}  // namespace dconv1d

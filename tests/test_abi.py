@@ -1,0 +1,92 @@
+"""The C-ABI library loads and exports every function include/dconv1d.h declares, and
+rejects invalid arguments on the host before any HIP call. CPU only: every call here
+fails validation (or is an empty batch), so no device work is issued."""
+import ctypes
+
+import pytest
+
+import normalisation_dilated_conv1d_amd as dc
+
+pytestmark = pytest.mark.skipif(not __import__("os").path.exists(dc.LIB_PATH),
+                                reason="libdconv1d.so not built")
+
+EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_bf16", "conv1d_groupnorm_fwd",
+            "dconv1d_last_error", "dconv1d_release", "dconv1d_timer_enable",
+            "dconv1d_timer_read"}
+
+FAKE_X = 0x10000000
+FAKE_OUT = 0x20000000
+FAKE_P = 0x30000000
+
+
+
+def test_header_declares_expected_functions():
+    assert set(dc.header_functions()) == EXPECTED
+
+
+def test_every_declared_symbol_is_exported():
+    lib = dc.load_library()
+    for name in dc.header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def _block(lib, x=FAKE_X, out=FAKE_OUT, N=2, C=16, L=512, d=128, eps=1e-5, b=FAKE_P, W=FAKE_P,
+           rm=FAKE_P, fn="prenorm_dconv1d_fwd"):
+    return getattr(lib, fn)(x, rm, FAKE_P, FAKE_P, FAKE_P, eps, W, b, out, N, C, L, d, None)
+
+
+@pytest.mark.parametrize("fn", ["prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), dc.DCONV1D_EINVAL), (dict(out=None), dc.DCONV1D_EINVAL),
+    (dict(W=None), dc.DCONV1D_EINVAL), (dict(rm=None), dc.DCONV1D_EINVAL),
+    (dict(N=-1), dc.DCONV1D_EINVAL), (dict(C=0), dc.DCONV1D_EINVAL),
+    (dict(L=0), dc.DCONV1D_EINVAL), (dict(d=0), dc.DCONV1D_EINVAL),
+    (dict(eps=-1.0), dc.DCONV1D_EINVAL), (dict(eps=float("nan")), dc.DCONV1D_EINVAL),
+    (dict(C=100000), dc.DCONV1D_EINVAL), (dict(C=16384, L=1 << 18), dc.DCONV1D_EINVAL),
+    (dict(out=FAKE_X), dc.DCONV1D_EALIAS), (dict(out="last_element"), dc.DCONV1D_EALIAS),
+    (dict(N=0), dc.DCONV1D_OK), (dict(N=0, x=None, out=None), dc.DCONV1D_OK),
+])
+def test_block_validation(fn, kw, code):
+    lib = dc.load_library()
+    elem = 2 if fn.endswith("bf16") else 4
+    nbytes = elem * 2 * 16 * 512
+    if kw.get("out") == "last_element":
+        kw = dict(out=FAKE_X + nbytes - elem)
+    assert _block(lib, fn=fn, **kw) == code
+    if code != dc.DCONV1D_OK:
+        assert lib.dconv1d_last_error().decode()
+
+
+def test_block_null_bias_is_valid_argument():
+    lib = dc.load_library()
+    # an empty batch with b = NULL passes validation and issues no work
+    assert _block(lib, N=0, b=None) == dc.DCONV1D_OK
+
+
+def _gn(lib, x=FAKE_X, out=FAKE_OUT, N=16, C_in=128, C_out=256, T=1024, G=32, p=1, dil=1,
+        eps=1e-5, W=FAKE_P):
+    return lib.conv1d_groupnorm_fwd(x, W, None, None, None, eps, G, out, N, C_in, C_out, T, p,
+                                    dil, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), dc.DCONV1D_EINVAL), (dict(W=None), dc.DCONV1D_EINVAL),
+    (dict(out=None), dc.DCONV1D_EINVAL), (dict(G=0), dc.DCONV1D_EINVAL),
+    (dict(G=3), dc.DCONV1D_EINVAL), (dict(T=0), dc.DCONV1D_EINVAL),
+    (dict(p=-1), dc.DCONV1D_EINVAL), (dict(dil=0), dc.DCONV1D_EINVAL),
+    (dict(T=4, p=0, dil=2), dc.DCONV1D_EINVAL), (dict(eps=float("inf")), dc.DCONV1D_EINVAL),
+    (dict(out=FAKE_X + 1024), dc.DCONV1D_EALIAS), (dict(N=0), dc.DCONV1D_OK),
+    (dict(N=0, x=None, out=None), dc.DCONV1D_OK),
+])
+def test_groupnorm_validation(kw, code):
+    lib = dc.load_library()
+    assert _gn(lib, **kw) == code
+
+
+def test_last_error_is_cleared_on_success():
+    lib = dc.load_library()
+    assert _block(lib, C=0) == dc.DCONV1D_EINVAL
+    assert b"C must be" in lib.dconv1d_last_error()
+    assert _block(lib, N=0) == dc.DCONV1D_OK
+    assert lib.dconv1d_last_error() == b""

@@ -1,0 +1,312 @@
+"""HIP path against the float64 CPU oracle, element by element, through the C ABI.
+
+Bars: float32 storage max |gpu - ref| / (1 + |ref|) <= 2e-4; bfloat16 storage <= 2e-2.
+Sizes span several tiles, ragged tails, multiple output-channel tiles, every dilation
+regime (contiguous taps to taps entirely in the padding) and the full benchmark
+workloads (compared in full where the oracle is quick, else on sampled outputs that
+include every boundary region)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import normalisation_dilated_conv1d_amd as dc
+import oracle
+from normalisation_dilated_conv1d_amd.inputs import (WORKLOADS, groupnorm_inputs,
+                                                      prenorm_inputs, seed_for)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 2e-4
+TOL_BF16 = 2e-2
+
+
+def announce(*parts):
+    print("[gpu-case]", *parts, file=sys.stderr, flush=True)
+
+
+def to_dev(p):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+
+
+def maxrel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
+
+
+def run_block(p, d, bf16=False, out=None):
+    q = to_dev(p)
+    fn = dc.prenorm_dconv1d_fwd_bf16 if bf16 else dc.prenorm_dconv1d_fwd
+    o = fn(q["x"], q["running_mean"], q["running_var"], q["gamma"], q["beta"], q["eps"], q["W"],
+           q["b"], d, out=out)
+    torch.cuda.synchronize()
+    return o
+
+
+def oracle_block(p, d):
+    return oracle.prenorm_block(p["x"], p["running_mean"], p["running_var"], p["gamma"],
+                                p["beta"], p["eps"], p["W"], p["b"], d)
+
+
+def sample_points(N, C, L, d, count, seed):
+    """Output points covering every boundary region plus random interior points."""
+    rng = np.random.default_rng(seed)
+    ts = {0, 1, L - 1, L - 2}
+    for base in (d, L - d):
+        for off in (-2, -1, 0, 1):
+            ts.add(base + off)
+    for tile in (64, 128):
+        for k in range(1, 4):
+            ts.update({k * tile - 1, k * tile})
+    ts = sorted(t for t in ts if 0 <= t < L)
+    pts = []
+    for t in ts:
+        for _ in range(4):
+            pts.append((int(rng.integers(N)), int(rng.integers(C)), t))
+    for co in (0, C - 1, min(255, C - 1), min(256, C - 1)):
+        pts.append((int(rng.integers(N)), co, int(rng.integers(L))))
+    while len(pts) < count:
+        pts.append((int(rng.integers(N)), int(rng.integers(C)), int(rng.integers(L))))
+    return pts
+
+
+# ----------------------------------------------------------------- small and medium shapes
+
+BLOCK_CASES = [
+    # (N, C, L, d)
+    (1, 1, 1, 1),
+    (1, 3, 7, 2),
+    (2, 16, 512, 128),       # the tiny workload's shape
+    (3, 48, 1000, 1),
+    (3, 48, 1000, 3),
+    (3, 48, 1000, 100),
+    (3, 48, 1000, 127),
+    (3, 48, 1000, 129),
+    (2, 48, 1000, 999),
+    (2, 48, 1000, 1000),     # d = L: only the centre tap
+    (2, 48, 1000, 5000),     # d > L
+    (2, 300, 700, 64),       # two output-channel tiles, C not a multiple of 32
+    (5, 256, 130, 7),
+    (8, 64, 8200, 128),      # 128-wide time tiles with a ragged tail
+    (2, 33, 257, 31),
+]
+
+
+@pytest.mark.parametrize("N,C,L,d", BLOCK_CASES)
+def test_block_f32_matches_oracle(N, C, L, d):
+    seed = 10_000 + N * 7 + C * 13 + L + d
+    announce("prenorm_dconv1d_fwd", (N, C, L, d), "seed", seed)
+    p = prenorm_inputs(N, C, L, seed)
+    got = run_block(p, d).cpu().numpy()
+    err = maxrel(got, oracle_block(p, d))
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("N,C,L,d", [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128),
+                                     (2, 300, 300, 300), (2, 16, 512, 128)])
+def test_block_bf16_matches_oracle(N, C, L, d):
+    seed = 20_000 + N + C + L + d
+    announce("prenorm_dconv1d_fwd_bf16", (N, C, L, d), "seed", seed)
+    p = prenorm_inputs(N, C, L, seed, bf16=True)
+    got = run_block(p, d, bf16=True).float().cpu().numpy()
+    err = maxrel(got, oracle_block(p, d))
+    assert err <= TOL_BF16, err
+
+
+def test_block_padding_trap():
+    """mean 0, gamma 1, beta +5: ReLU(BN(0)) = 5; padded taps must still be exactly 0."""
+    N, C, L, d = 2, 64, 600, 100
+    announce("prenorm_dconv1d_fwd padding trap", (N, C, L, d))
+    p = prenorm_inputs(N, C, L, 31)
+    p["running_mean"] = torch.zeros(C)
+    p["running_var"] = torch.ones(C)
+    p["gamma"] = torch.ones(C)
+    p["beta"] = torch.full((C,), 5.0)
+    got = run_block(p, d).cpu().numpy()
+    err = maxrel(got, oracle_block(p, d))
+    assert err <= TOL_F32, err
+
+
+def test_block_zero_weights_exact():
+    """W = 0: out = x + b, exactly (one float32 add)."""
+    N, C, L, d = 2, 40, 300, 9
+    announce("prenorm_dconv1d_fwd zero W", (N, C, L, d))
+    p = prenorm_inputs(N, C, L, 32)
+    p["W"] = torch.zeros(C, C, 3)
+    got = run_block(p, d).cpu()
+    exp = p["x"] + p["b"][None, :, None]
+    assert torch.equal(got, exp)
+
+
+def test_block_null_bias():
+    N, C, L, d = 2, 40, 300, 9
+    announce("prenorm_dconv1d_fwd b=NULL", (N, C, L, d))
+    p = prenorm_inputs(N, C, L, 33)
+    p["b"] = None
+    err = maxrel(run_block(p, d).cpu().numpy(), oracle_block(p, d))
+    assert err <= TOL_F32, err
+
+
+def test_block_empty_batch():
+    announce("prenorm_dconv1d_fwd N=0")
+    p = prenorm_inputs(0, 16, 64, 34)
+    assert run_block(p, 4).shape == (0, 16, 64)
+    assert run_block(prenorm_inputs(0, 16, 64, 34, bf16=True), 4, bf16=True).shape == (0, 16, 64)
+    g = groupnorm_inputs(0, 8, 16, 20, 35)
+    assert run_gn(g, 4, 1, 1).shape == (0, 16, 20)
+
+
+def test_block_guard_band_and_stream():
+    """Writes stay inside out (sentinels around it survive) and work runs on a
+    non-default stream."""
+    N, C, L, d = 2, 64, 777, 33
+    announce("prenorm_dconv1d_fwd guard band", (N, C, L, d))
+    p = prenorm_inputs(N, C, L, 35)
+    q = to_dev(p)
+    n = N * C * L
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), 12345.0, device="cuda")
+    out = buf[guard:guard + n].view(N, C, L)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dc.prenorm_dconv1d_fwd(q["x"], q["running_mean"], q["running_var"], q["gamma"],
+                               q["beta"], q["eps"], q["W"], q["b"], d, out=out)
+    s.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[:guard] == 12345.0) and torch.all(b[guard + n:] == 12345.0)
+    err = maxrel(out.cpu().numpy(), oracle_block(p, d))
+    assert err <= TOL_F32, err
+
+
+def test_block_deterministic():
+    N, C, L, d = 4, 256, 2048, 128
+    announce("prenorm_dconv1d_fwd determinism", (N, C, L, d))
+    q = to_dev(prenorm_inputs(N, C, L, 36))
+    outs = [dc.prenorm_dconv1d_fwd(q["x"], q["running_mean"], q["running_var"], q["gamma"],
+                                   q["beta"], q["eps"], q["W"], q["b"], d) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_block_alias_rejected():
+    q = to_dev(prenorm_inputs(1, 8, 32, 37))
+    with pytest.raises(dc.Dconv1dError) as e:
+        dc.prenorm_dconv1d_fwd(q["x"], q["running_mean"], q["running_var"], q["gamma"],
+                               q["beta"], q["eps"], q["W"], q["b"], 2, out=q["x"])
+    assert e.value.code == dc.DCONV1D_EALIAS
+
+
+# ----------------------------------------------------------------- GroupNorm sibling
+
+GN_CASES = [
+    # (N, C_in, C_out, T, G, padding, dilation, bias, affine)
+    (2, 40, 96, 333, 12, 1, 1, False, True),
+    (2, 40, 96, 333, 12, 1, 1, True, True),
+    (2, 40, 96, 333, 12, 1, 1, False, False),
+    (1, 16, 32, 77, 1, 3, 2, True, True),
+    (1, 16, 32, 77, 32, 0, 1, False, True),
+    (2, 64, 300, 150, 3, 1, 1, False, True),     # two output-channel tiles
+    (3, 8, 16, 5, 4, 2, 3, False, True),         # T_out = 3
+    (4, 128, 256, 1023, 32, 1, 1, False, True),  # ragged time tail
+]
+
+
+def run_gn(p, G, padding, dilation):
+    q = to_dev(p)
+    o = dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"], G,
+                                padding, dilation)
+    torch.cuda.synchronize()
+    return o
+
+
+def oracle_gn(p, G, padding, dilation):
+    return oracle.conv_groupnorm(p["x"], p["W"], p["bias"], p["gamma"], p["beta"], p["eps"], G,
+                                 padding, dilation)
+
+
+@pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil,bias,affine", GN_CASES)
+def test_groupnorm_matches_oracle(N, C_in, C_out, T, G, pad, dil, bias, affine):
+    seed = 30_000 + N + C_in + C_out + T + G + pad + dil
+    announce("conv1d_groupnorm_fwd", (N, C_in, C_out, T, G, pad, dil, bias, affine), "seed", seed)
+    p = groupnorm_inputs(N, C_in, C_out, T, seed, with_bias=bias)
+    if not affine:
+        p["gamma"] = None
+        p["beta"] = None
+    got = run_gn(p, G, pad, dil).cpu().numpy()
+    err = maxrel(got, oracle_gn(p, G, pad, dil))
+    assert err <= TOL_F32, err
+
+
+def test_groupnorm_deterministic():
+    w = WORKLOADS[3].dims
+    announce("conv1d_groupnorm_fwd determinism", w)
+    q = to_dev(groupnorm_inputs(w["N"], w["C_in"], w["C_out"], w["T"], seed_for(3, 1)))
+    outs = []
+    for _ in range(5):
+        outs.append(dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"],
+                                            q["eps"], w["G"], w["padding"], w["dilation"]))
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+# ----------------------------------------------------------------- full benchmark workloads
+
+def test_workload0_tiny():
+    w = WORKLOADS[0].dims
+    announce("workload 0", w)
+    p = prenorm_inputs(w["N"], w["C"], w["L"], seed_for(0))
+    err = maxrel(run_block(p, w["d"]).cpu().numpy(), oracle_block(p, w["d"]))
+    assert err <= TOL_F32, err
+
+
+def test_workload1_full():
+    """N=32, C=256, L=4096, d=128: every output against the oracle."""
+    w = WORKLOADS[1].dims
+    announce("workload 1 full compare", w)
+    p = prenorm_inputs(w["N"], w["C"], w["L"], seed_for(1))
+    got = run_block(p, w["d"]).cpu().numpy()
+    err = maxrel(got, oracle_block(p, w["d"]))
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("d", WORKLOADS[2].dims["ds"])
+def test_workload2_dilation_sweep(d):
+    w = WORKLOADS[2].dims
+    announce("workload 2 sampled compare", w, "d", d)
+    p = prenorm_inputs(w["N"], w["C"], w["L"], seed_for(2, d))
+    got = run_block(p, d).cpu()
+    pts = sample_points(w["N"], w["C"], w["L"], d, 3000, d)
+    ref = oracle.prenorm_block_points(p["x"], p["running_mean"], p["running_var"], p["gamma"],
+                                      p["beta"], p["eps"], p["W"], p["b"], d, pts)
+    g = np.array([float(got[n, c, t]) for (n, c, t) in pts])
+    err = maxrel(g, ref)
+    assert err <= TOL_F32, err
+
+
+def test_workload3_groupnorm_full():
+    w = WORKLOADS[3].dims
+    announce("workload 3 full compare", w)
+    p = groupnorm_inputs(w["N"], w["C_in"], w["C_out"], w["T"], seed_for(3))
+    got = run_gn(p, w["G"], w["padding"], w["dilation"]).cpu().numpy()
+    err = maxrel(got, oracle_gn(p, w["G"], w["padding"], w["dilation"]))
+    assert err <= TOL_F32, err
+
+
+def test_workload4_bf16_sampled():
+    w = WORKLOADS[4].dims
+    announce("workload 4 sampled compare", w)
+    p = prenorm_inputs(w["N"], w["C"], w["L"], seed_for(4), bf16=True)
+    got = run_block(p, w["d"], bf16=True).cpu()
+    pts = sample_points(w["N"], w["C"], w["L"], w["d"], 3000, 4)
+    ref = oracle.prenorm_block_points(p["x"], p["running_mean"], p["running_var"], p["gamma"],
+                                      p["beta"], p["eps"], p["W"], p["b"], w["d"], pts)
+    g = np.array([float(got[n, c, t].float()) for (n, c, t) in pts])
+    err = maxrel(g, ref)
+    assert err <= TOL_BF16, err
