@@ -79,14 +79,18 @@ template <int TT, bool BN, int EPI, typename XT>
 __global__ void __launch_bounds__(NTHREADS)
 conv_f32_kernel(ConvF32Args a) {
   constexpr int NJ = TT / 32;                    // 32-column MFMA blocks per wave
-  constexpr int XPT = KC * TT / NTHREADS;        // staged values per thread per chunk
-  constexpr int RPP = NTHREADS / TT;             // rows covered by one pass of the workgroup
-  constexpr int PITCH = TT + 8;                  // LDS row pitch (floats); +8 staggers the
-                                                 // two half-wave rows onto different banks
-  __shared__ float zs[2][KC * PITCH];
+  constexpr int CPT = TT / 64;                   // staged columns per thread
+  constexpr int RPW = KC / 4;                    // staged rows per wave (8)
+  constexpr int XPT = RPW * CPT;                 // staged values per thread per chunk
+  // LDS row layout: column c lives at (c % 32) * NJ + c / 32, so lane lc finds its NJ
+  // B values (columns lc, 32 + lc, ...) contiguous and reads them with one wide load.
+  // Pitch TT + 8 puts the rows read by the two half-waves (4 apart) 32 banks apart.
+  constexpr int PITCH = TT + 8;
+  typedef float bvec __attribute__((ext_vector_type(NJ)));
+  __shared__ __attribute__((aligned(16))) float zs[2][KC * PITCH];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int h = l >> 5;
   const int lc = l & 31;
@@ -103,11 +107,6 @@ conv_f32_kernel(ConvF32Args a) {
   const int t0 = tt * TT;
 
   const XT* __restrict__ xn = reinterpret_cast<const XT*>(a.x) + (size_t)n * a.C_in * a.L_in;
-
-  // Staging map: thread covers column `col` of rows r0, r0 + RPP, ... (r0 is wave-uniform).
-  const int col = tid % TT;
-  const int r0 = __builtin_amdgcn_readfirstlane(tid / TT);
-
   const f32x4* __restrict__ Wp4 = reinterpret_cast<const f32x4*>(a.Wp);
   const int cb0 = (ct * CO_TILE_F32) / 32 + 2 * w;
 
@@ -119,33 +118,53 @@ conv_f32_kernel(ConvF32Args a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nj][r] = 0.f;
 
+  // Staging map: wave w stages rows [8w, 8w + 8) of the chunk; lane l covers columns
+  // l + 64*j. Every load instruction reads 64 consecutive time steps of one row.
   float xr[XPT];
-  f32x4 wc[4][2], wn[4][2];
+  float sc[RPW], sh[RPW];
+  f32x4 wA[4][2], wB[4][2];
 
+  // Loads are branch-free: the address is clamped into the tensor and the value is
+  // replaced by 0 afterwards where the tap falls in the padding, so the compiler sees
+  // a fixed number of loads per chunk and can keep prefetches in flight. The folded BN
+  // parameters cover the padded channel range, so they need no clamp.
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
-    const int ts = t0 + col + k * a.dil - a.pad;
-    const bool tok = ts >= 0 && ts < a.L_in;
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int ci = c * KC + r0 + RPP * i;
-      xr[i] = (tok && ci < a.C_in) ? to_f32(xn[ci * a.L_in + ts]) : 0.f;
+    for (int j = 0; j < CPT; ++j) {
+      const int ts = t0 + l + 64 * j + k * a.dil - a.pad;
+      const int tsc = min(max(ts, 0), a.L_in - 1);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int ci = min(c * KC + RPW * w + i, a.C_in - 1);
+        xr[i * CPT + j] = to_f32(xn[ci * a.L_in + tsc]);
+      }
+    }
+    if (BN) {
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        sc[i] = a.scale[c * KC + RPW * w + i];
+        sh[i] = a.shift[c * KC + RPW * w + i];
+      }
     }
   };
   auto store_z = [&](int q, float* dst) {
     const int c = q / 3, k = q - 3 * c;
-    const int ts = t0 + col + k * a.dil - a.pad;
-    const bool tok = ts >= 0 && ts < a.L_in;
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int row = r0 + RPP * i;
-      const int ci = c * KC + row;
-      float v = xr[i];
-      if (BN) {
-        // z = ReLU(scale*x + shift) inside the input, exactly 0 in the padding.
-        v = (tok && ci < a.C_in) ? fmaxf(fmaf(v, a.scale[ci], a.shift[ci]), 0.f) : 0.f;
+    for (int j = 0; j < CPT; ++j) {
+      const int col = l + 64 * j;
+      const int ts = t0 + col + k * a.dil - a.pad;
+      const bool tok = ts >= 0 && ts < a.L_in;
+      const int pos = (col & 31) * NJ + (col >> 5);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int row = RPW * w + i;
+        const bool ok = tok && (c * KC + row < a.C_in);
+        float v = xr[i * CPT + j];
+        // z = ReLU(scale*x + shift) inside the input, exactly 0 in the padding
+        if (BN) v = fmaxf(fmaf(v, sc[i], sh[i]), 0.f);
+        dst[row * PITCH + pos] = ok ? v : 0.f;
       }
-      dst[row * PITCH + col] = v;
     }
   };
   auto load_w = [&](int q, f32x4 (&dst)[4][2]) {
@@ -155,45 +174,61 @@ conv_f32_kernel(ConvF32Args a) {
       for (int mb = 0; mb < 2; ++mb)
         dst[g][mb] = Wp4[((q * 4 + g) * a.NCB + cb0 + mb) * 64 + l];
   };
-
-  load_x(0);
-  load_w(0, wc);
-  store_z(0, zs[0]);
-  __syncthreads();
-
-  for (int q = 0; q < a.Q; ++q) {
-    const bool more = q + 1 < a.Q;
-    if (more) {
-      load_x(q + 1);
-      load_w(q + 1, wn);
-    }
-    const float* zb = zs[q & 1];
+  // B operands of row group g (4 MFMA steps): one wide LDS read per step.
+  auto load_b = [&](const float* zb, int g, bvec (&dst)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dst[u] = *reinterpret_cast<const bvec*>(zb + (8 * g + 4 * h + u) * PITCH + lc * NJ);
+  };
+  auto compute = [&](const float* zb, const f32x4 (&wc)[4][2]) {
+    bvec bv[2][4];
+    load_b(zb, 0, bv[0]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      if (g + 1 < 4) load_b(zb, g + 1, bv[(g + 1) & 1]);  // one group ahead
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = 8 * g + 4 * h + u;
-        float bv[NJ];
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) bv[nj] = zb[row * PITCH + 32 * nj + lc];
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const float av = wc[g][mb][u];
 #pragma unroll
           for (int nj = 0; nj < NJ; ++nj)
-            acc[mb][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv[nj], acc[mb][nj], 0, 0, 0);
+            acc[mb][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv[g & 1][u][nj],
+                                                                acc[mb][nj], 0, 0, 0);
         }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      store_z(q + 1, zs[(q + 1) & 1]);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) wc[g][mb] = wn[g][mb];
-    }
+  };
+
+  // Two chunks per trip with ping-pong weight registers (wA: even chunks, LDS buffer 0;
+  // wB: odd chunks, buffer 1), so no register copies cross the loop edge. The prefetch
+  // index is clamped to the last chunk, which keeps the body free of branches; at most
+  // one chunk is staged twice. sched_barrier pins each chunk's prefetch loads ahead of
+  // the MFMA block; left alone, the scheduler sinks them to its end and their latency
+  // is exposed every chunk.
+  const int Q = a.Q;
+  load_x(0);
+  load_w(0, wA);
+  store_z(0, zs[0]);
+  __syncthreads();
+  int q = 0;
+  for (; q + 1 < Q; q += 2) {
+    load_x(q + 1);
+    load_w(q + 1, wB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(zs[0], wA);
+    store_z(q + 1, zs[1]);
+    __syncthreads();
+    const int qn = min(q + 2, Q - 1);
+    load_x(qn);
+    load_w(qn, wA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(zs[1], wB);
+    store_z(qn, zs[0]);
     __syncthreads();
   }
+  if (q < Q) compute(zs[0], wA);  // odd chunk count: the last chunk is already staged
 
   // Epilogue. Accumulator register r of block (mb, nj) holds output channel
   // 32*mb + 8*(r/4) + 4*h + r%4 (within the wave's 64) and time 32*nj + lc.
