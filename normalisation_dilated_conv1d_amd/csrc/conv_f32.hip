@@ -76,7 +76,7 @@ __device__ __forceinline__ void from_f32(float v, uint16_t* dst) {
 }
 
 template <int TT, bool BN, int EPI, typename XT>
-__global__ void __launch_bounds__(NTHREADS)
+__global__ void __launch_bounds__(NTHREADS, 2)
 conv_f32_kernel(ConvF32Args a) {
   constexpr int NJ = TT / 32;                    // 32-column MFMA blocks per wave
   constexpr int CPT = TT / 64;                   // staged columns per thread
@@ -122,11 +122,10 @@ conv_f32_kernel(ConvF32Args a) {
   // l + 64*j. Every load instruction reads 64 consecutive time steps of one row.
   float xr[XPT];
   float sc[RPW], sh[RPW];
-  f32x4 wA[4][2], wB[4][2];
 
   // Loads are branch-free: the address is clamped into the tensor and the value is
-  // replaced by 0 afterwards where the tap falls in the padding, so the compiler sees
-  // a fixed number of loads per chunk and can keep prefetches in flight. The folded BN
+  // masked to 0 afterwards where the tap falls in the padding, so the compiler sees a
+  // fixed number of loads per chunk and keeps prefetches in flight. The folded BN
   // parameters cover the padded channel range, so they need no clamp.
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
@@ -154,25 +153,29 @@ conv_f32_kernel(ConvF32Args a) {
     for (int j = 0; j < CPT; ++j) {
       const int col = l + 64 * j;
       const int ts = t0 + col + k * a.dil - a.pad;
-      const bool tok = ts >= 0 && ts < a.L_in;
+      // all-ones inside the input, 0 in the padding; kept opaque to the optimiser so
+      // the masking stays an AND instead of turning into a divergent branch
+      uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
+      asm volatile("" : "+v"(tkeep));
       const int pos = (col & 31) * NJ + (col >> 5);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int row = RPW * w + i;
-        const bool ok = tok && (c * KC + row < a.C_in);
+        const uint32_t keep = (c * KC + row < a.C_in) ? tkeep : 0u;
         float v = xr[i * CPT + j];
         // z = ReLU(scale*x + shift) inside the input, exactly 0 in the padding
         if (BN) v = fmaxf(fmaf(v, sc[i], sh[i]), 0.f);
-        dst[row * PITCH + pos] = ok ? v : 0.f;
+        dst[row * PITCH + pos] = __uint_as_float(__float_as_uint(v) & keep);
       }
     }
   };
-  auto load_w = [&](int q, f32x4 (&dst)[4][2]) {
+  // A operands of row group G = 4*chunk + g (4 MFMA steps, both 32-channel blocks).
+  // Clamped to the last group so the prefetch past the end stays in bounds.
+  const int n_groups = 4 * a.Q;
+  auto load_w = [&](int G, f32x4 (&dst)[2]) {
+    G = min(G, n_groups - 1);
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        dst[g][mb] = Wp4[((q * 4 + g) * a.NCB + cb0 + mb) * 64 + l];
+    for (int mb = 0; mb < 2; ++mb) dst[mb] = Wp4[(G * a.NCB + cb0 + mb) * 64 + l];
   };
   // B operands of row group g (4 MFMA steps): one wide LDS read per step.
   auto load_b = [&](const float* zb, int g, bvec (&dst)[4]) {
@@ -180,55 +183,65 @@ conv_f32_kernel(ConvF32Args a) {
     for (int u = 0; u < 4; ++u)
       dst[u] = *reinterpret_cast<const bvec*>(zb + (8 * g + 4 * h + u) * PITCH + lc * NJ);
   };
-  auto compute = [&](const float* zb, const f32x4 (&wc)[4][2]) {
-    bvec bv[2][4];
+
+  // Weights rotate through a ring of 4 register slots, loaded two row groups (half a
+  // chunk) ahead; slot = group index mod 4 is a compile-time constant because a chunk
+  // is exactly 4 groups.
+  f32x4 wr[4][2];
+  bvec bv[2][4];
+
+  // One chunk of MFMAs on LDS buffer zb, chunk index q (group base 4q). `mid` runs
+  // between row groups 1 and 2: it stages the next chunk into the other LDS buffer
+  // (free since the last barrier) while this chunk's MFMAs are still in flight.
+  auto compute = [&](const float* zb, int q, auto&& mid) {
     load_b(zb, 0, bv[0]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (g + 1 < 4) load_b(zb, g + 1, bv[(g + 1) & 1]);  // one group ahead
+      load_w(4 * q + g + 2, wr[(g + 2) & 3]);
+      if (g + 1 < 4) load_b(zb, g + 1, bv[(g + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const float av = wc[g][mb][u];
+          const float av = wr[g][mb][u];
 #pragma unroll
           for (int nj = 0; nj < NJ; ++nj)
             acc[mb][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv[g & 1][u][nj],
                                                                 acc[mb][nj], 0, 0, 0);
         }
       __builtin_amdgcn_sched_barrier(0);
+      if (g == 1) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
-  // Two chunks per trip with ping-pong weight registers (wA: even chunks, LDS buffer 0;
-  // wB: odd chunks, buffer 1), so no register copies cross the loop edge. The prefetch
+  // Two chunks per trip (LDS buffer 0 for even chunks, 1 for odd). The staged chunk
   // index is clamped to the last chunk, which keeps the body free of branches; at most
-  // one chunk is staged twice. sched_barrier pins each chunk's prefetch loads ahead of
-  // the MFMA block; left alone, the scheduler sinks them to its end and their latency
-  // is exposed every chunk.
+  // one chunk is staged twice. sched_barrier pins every prefetch ahead of the MFMAs
+  // that follow it; left alone, the scheduler sinks loads to the end of the MFMA block
+  // and their latency is exposed.
   const int Q = a.Q;
+  load_w(0, wr[0]);
+  load_w(1, wr[1]);
   load_x(0);
-  load_w(0, wA);
   store_z(0, zs[0]);
   __syncthreads();
   int q = 0;
   for (; q + 1 < Q; q += 2) {
     load_x(q + 1);
-    load_w(q + 1, wB);
     __builtin_amdgcn_sched_barrier(0);
-    compute(zs[0], wA);
-    store_z(q + 1, zs[1]);
+    compute(zs[0], q, [&] { store_z(q + 1, zs[1]); });
     __syncthreads();
     const int qn = min(q + 2, Q - 1);
     load_x(qn);
-    load_w(qn, wA);
     __builtin_amdgcn_sched_barrier(0);
-    compute(zs[1], wB);
-    store_z(qn, zs[0]);
+    compute(zs[1], q + 1, [&] { store_z(qn, zs[0]); });
     __syncthreads();
   }
-  if (q < Q) compute(zs[0], wA);  // odd chunk count: the last chunk is already staged
+  if (q < Q) compute(zs[0], q, [] {});  // odd chunk count: the last chunk is staged
 
   // Epilogue. Accumulator register r of block (mb, nj) holds output channel
   // 32*mb + 8*(r/4) + 4*h + r%4 (within the wave's 64) and time 32*nj + lc.
