@@ -193,7 +193,7 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   a.L_out = Li;
   a.pad = d_eff;
   a.dil = d_eff;
-  a.NCB = Cout_pad / 32;
+  a.NCB = Cout_pad / 16;
   a.Q = 3 * Cin_pad / KC;
   a.n_tt = n_tt;
   a.n_ct = n_ct;
@@ -295,7 +295,7 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
   a.L_out = Lo;
   a.pad = (int)padding;
   a.dil = (int)dilation;
-  a.NCB = Cout_pad / 32;
+  a.NCB = Cout_pad / 16;
   a.Q = 3 * Cin_pad / KC;
   a.n_tt = n_tt;
   a.n_ct = n_ct;

@@ -15,26 +15,30 @@
 // Work split
 //   workgroup  = one sample n, 256 output channels (co tile), TT time steps (t tile);
 //                4 waves, wave w owns output channels [64w, 64w+64) of the co tile and
-//                all TT time steps: 2 x (TT/32) MFMA 32x32 accumulator blocks.
+//                all TT time steps: 4 x (TT/16) MFMA 16x16 accumulator blocks.
 //   K loop     = chunks of 32 input channels of one tap, ordered (ci-block, tap) so
 //                that the three taps of a channel block are staged back to back and hit
 //                the same L2 lines.
 //   B operand  = the activation tile z[32][TT], staged through LDS once per chunk by
 //                all 256 threads (global loads coalesced along t, BN+ReLU applied in
 //                registers, zero outside [0, L_in)), double-buffered, one barrier per
-//                chunk.
+//                chunk; the staging of chunk q+1 runs in the middle of chunk q's MFMAs.
 //   A operand  = the weights, read straight from global memory into registers: the
 //                repack kernel stores them in the exact lane order of the MFMA A operand,
 //                so each lane fetches 4 consecutive K values with one 16-byte load and
 //                each wave reads 1 KB contiguous per load. No LDS for W: no two waves of
 //                a workgroup use the same weights.
-//   MFMA       = v_mfma_f32_32x32x2_f32 (full float32 products and accumulation).
+//   MFMA       = v_mfma_f32_16x16x4_f32 (full float32 products and accumulation). On
+//                MI355X it sustains a higher clock under load than the 32x32x2 form
+//                (measured ~155 vs ~145 TFLOP/s in a register-only loop).
+//   Occupancy  = at most 256 VGPRs, so two workgroups share each CU (two waves per
+//                SIMD) and hide each other's barriers, staging and epilogue.
 //
-// K permutation inside a chunk: the 32 rows r of a chunk are split as r = 8g + 4h + u
-// (g: 4 groups, h: the lane's half-wave, u: 4 steps). MFMA step (g, u) uses rows
-// 8g + u (lanes 0-31) and 8g + 4 + u (lanes 32-63) as its two K values, so a lane's
-// four A values for steps u = 0..3 are contiguous in the repacked weights. A and B use
-// the same permutation, so the sum over K is unchanged.
+// K permutation inside a chunk: the 32 rows r of a chunk are split as r = 16g + 4q + u
+// (g: two 16-row groups, q = lane/16: the lane's quarter-wave, u: 4 steps). MFMA step
+// (g, u) gives quarter-wave q row 16g + 4q + u as its K value, so a lane's four A
+// values for steps u = 0..3 are contiguous in the repacked weights. A and B use the
+// same permutation, so the sum over K is unchanged.
 //
 // Workgroup order is XCD-aware: the hardware sends workgroup b to XCD b % 8, so the
 // logical tile index is remapped to give every XCD one contiguous range of tiles; the
@@ -44,17 +48,15 @@
 
 namespace dconv1d {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Sum over the 32 lanes of each half-wave with ds_swizzle butterflies (xor 16..1).
+// Sum over the 16 lanes of each quarter-wave with ds_swizzle butterflies (xor 8..1).
 // Every lane ends with the same, order-fixed value.
 template <int XOR>
 __device__ __forceinline__ float swz_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (XOR << 10) | 0x1F));
 }
-__device__ __forceinline__ float halfwave_sum(float v) {
-  v += swz_xor<16>(v);
+__device__ __forceinline__ float quarterwave_sum(float v) {
   v += swz_xor<8>(v);
   v += swz_xor<4>(v);
   v += swz_xor<2>(v);
@@ -78,24 +80,23 @@ __device__ __forceinline__ void from_f32(float v, uint16_t* dst) {
 template <int TT, bool BN, int EPI, typename XT>
 __global__ void __launch_bounds__(NTHREADS, 2)
 conv_f32_kernel(ConvF32Args a) {
-  constexpr int NJ = TT / 32;                    // 32-column MFMA blocks per wave
+  constexpr int NB = TT / 16;                    // 16-column MFMA blocks per wave
+  constexpr int NQ = NB / 4;                     // 16-byte LDS reads per MFMA step
   constexpr int CPT = TT / 64;                   // staged columns per thread
   constexpr int RPW = KC / 4;                    // staged rows per wave (8)
   constexpr int XPT = RPW * CPT;                 // staged values per thread per chunk
-  // LDS row layout: column c lives at (c % 32) * NJ + c / 32, so lane lc finds its NJ
-  // B values (columns lc, 32 + lc, ...) contiguous and reads them with one wide load.
-  // Pitch TT + 8 puts the rows read by the two half-waves (4 apart) 32 banks apart.
-  constexpr int PITCH = TT + 8;
-  typedef float bvec __attribute__((ext_vector_type(NJ)));
+  // LDS row layout: within each 64-column quarter, column c lives at
+  // (c % 16) * 4 + (c % 64) / 16, so lane l reads its 4 B values (columns l%16 + 16*nb)
+  // with one 16-byte load and the 16 lanes of a quarter-wave read 256 contiguous bytes.
+  constexpr int PITCH = TT + 4;
   __shared__ __attribute__((aligned(16))) float zs[2][KC * PITCH];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
-  const int h = l >> 5;
-  const int lc = l & 31;
+  const int lq = l >> 4;     // quarter-wave: selects the K row inside an MFMA step
+  const int l16 = l & 15;
 
-  // XCD-aware tile order.
   const int nwg = gridDim.x;
   const int b = blockIdx.x;
   const int per = nwg >> 3, rem = nwg & 7, xcd = b & 7;
@@ -108,25 +109,19 @@ conv_f32_kernel(ConvF32Args a) {
 
   const XT* __restrict__ xn = reinterpret_cast<const XT*>(a.x) + (size_t)n * a.C_in * a.L_in;
   const f32x4* __restrict__ Wp4 = reinterpret_cast<const f32x4*>(a.Wp);
-  const int cb0 = (ct * CO_TILE_F32) / 32 + 2 * w;
+  const int cb0 = (ct * CO_TILE_F32) / 16 + 4 * w;   // first 16-channel block of the wave
 
-  f32x16 acc[2][NJ];
+  f32x4 acc[4][NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nj = 0; nj < NJ; ++nj)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][nj][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[mb][nb][r] = 0.f;
 
-  // Staging map: wave w stages rows [8w, 8w + 8) of the chunk; lane l covers columns
-  // l + 64*j. Every load instruction reads 64 consecutive time steps of one row.
   float xr[XPT];
   float sc[RPW], sh[RPW];
 
-  // Loads are branch-free: the address is clamped into the tensor and the value is
-  // masked to 0 afterwards where the tap falls in the padding, so the compiler sees a
-  // fixed number of loads per chunk and keeps prefetches in flight. The folded BN
-  // parameters cover the padded channel range, so they need no clamp.
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
 #pragma unroll
@@ -153,79 +148,66 @@ conv_f32_kernel(ConvF32Args a) {
     for (int j = 0; j < CPT; ++j) {
       const int col = l + 64 * j;
       const int ts = t0 + col + k * a.dil - a.pad;
-      // all-ones inside the input, 0 in the padding; kept opaque to the optimiser so
-      // the masking stays an AND instead of turning into a divergent branch
       uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
       asm volatile("" : "+v"(tkeep));
-      const int pos = (col & 31) * NJ + (col >> 5);
+      const int pos = 64 * j + (col & 15) * 4 + ((col & 63) >> 4);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int row = RPW * w + i;
         const uint32_t keep = (c * KC + row < a.C_in) ? tkeep : 0u;
         float v = xr[i * CPT + j];
-        // z = ReLU(scale*x + shift) inside the input, exactly 0 in the padding
         if (BN) v = fmaxf(fmaf(v, sc[i], sh[i]), 0.f);
         dst[row * PITCH + pos] = __uint_as_float(__float_as_uint(v) & keep);
       }
     }
   };
-  // A operands of row group G = 4*chunk + g (4 MFMA steps, both 32-channel blocks).
-  // Clamped to the last group so the prefetch past the end stays in bounds.
-  const int n_groups = 4 * a.Q;
-  auto load_w = [&](int G, f32x4 (&dst)[2]) {
+  // A operands of 16-row group G = 2*chunk + g: 4 float4 (one per 16-channel block),
+  // each holding the lane's 4 MFMA steps.
+  const int n_groups = 2 * a.Q;
+  auto load_w = [&](int G, f32x4 (&dst)[4]) {
     G = min(G, n_groups - 1);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) dst[mb] = Wp4[(G * a.NCB + cb0 + mb) * 64 + l];
+    for (int mb = 0; mb < 4; ++mb) dst[mb] = Wp4[(G * a.NCB + cb0 + mb) * 64 + l];
   };
-  // B operands of row group g (4 MFMA steps): one wide LDS read per step.
-  auto load_b = [&](const float* zb, int g, bvec (&dst)[4]) {
+  // B operands of MFMA step s (row 16*(s/4) + 4*lq + s%4).
+  auto load_b = [&](const float* zb, int s, f32x4 (&dst)[NQ]) {
+    const float* p = zb + (16 * (s >> 2) + 4 * lq + (s & 3)) * PITCH + l16 * 4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      dst[u] = *reinterpret_cast<const bvec*>(zb + (8 * g + 4 * h + u) * PITCH + lc * NJ);
+    for (int m = 0; m < NQ; ++m) dst[m] = *reinterpret_cast<const f32x4*>(p + 64 * m);
   };
 
-  // Weights rotate through a ring of 4 register slots, loaded two row groups (half a
-  // chunk) ahead; slot = group index mod 4 is a compile-time constant because a chunk
-  // is exactly 4 groups.
-  f32x4 wr[4][2];
-  bvec bv[2][4];
+  f32x4 wr[2][4];
+  f32x4 bv[2][NQ];
 
-  // One chunk of MFMAs on LDS buffer zb, chunk index q (group base 4q). `mid` runs
-  // between row groups 1 and 2: it stages the next chunk into the other LDS buffer
-  // (free since the last barrier) while this chunk's MFMAs are still in flight.
   auto compute = [&](const float* zb, int q, auto&& mid) {
     load_b(zb, 0, bv[0]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      load_w(4 * q + g + 2, wr[(g + 2) & 3]);
-      if (g + 1 < 4) load_b(zb, g + 1, bv[(g + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < 2; ++g) {
+      load_w(2 * q + g + 1, wr[(g + 1) & 1]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
+        const int s = 4 * g + u;
+        if (s + 1 < 8) load_b(zb, s + 1, bv[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 4; ++mb) {
           const float av = wr[g][mb][u];
 #pragma unroll
-          for (int nj = 0; nj < NJ; ++nj)
-            acc[mb][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv[g & 1][u][nj],
-                                                                acc[mb][nj], 0, 0, 0);
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[s & 1][nb >> 2][nb & 3],
+                                                               acc[mb][nb], 0, 0, 0);
         }
-      __builtin_amdgcn_sched_barrier(0);
-      if (g == 1) {
-        mid();
         __builtin_amdgcn_sched_barrier(0);
+        if (s == 3) {
+          mid();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
 
-  // Two chunks per trip (LDS buffer 0 for even chunks, 1 for odd). The staged chunk
-  // index is clamped to the last chunk, which keeps the body free of branches; at most
-  // one chunk is staged twice. sched_barrier pins every prefetch ahead of the MFMAs
-  // that follow it; left alone, the scheduler sinks loads to the end of the MFMA block
-  // and their latency is exposed.
   const int Q = a.Q;
   load_w(0, wr[0]);
-  load_w(1, wr[1]);
   load_x(0);
   store_z(0, zs[0]);
   __syncthreads();
@@ -241,27 +223,25 @@ conv_f32_kernel(ConvF32Args a) {
     compute(zs[1], q + 1, [&] { store_z(qn, zs[0]); });
     __syncthreads();
   }
-  if (q < Q) compute(zs[0], q, [] {});  // odd chunk count: the last chunk is staged
+  if (q < Q) compute(zs[0], q, [] {});
 
-  // Epilogue. Accumulator register r of block (mb, nj) holds output channel
-  // 32*mb + 8*(r/4) + 4*h + r%4 (within the wave's 64) and time 32*nj + lc.
+  // Epilogue. Accumulator register r of block (mb, nb) holds output channel
+  // 16*mb + 4*lq + r (within the wave's 64) and time 16*nb + l16.
   XT* __restrict__ outn = reinterpret_cast<XT*>(a.out) + (size_t)n * a.C_out * a.L_out;
-  const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * h;
+  const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
   if (EPI == EPI_RESIDUAL) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int co = co_base + 32 * mb + 8 * (r >> 2) + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int co = co_base + 16 * mb + r;
         if (co < a.C_out) {
           const float bco = a.bias ? a.bias[co] : 0.f;
 #pragma unroll
-          for (int nj = 0; nj < NJ; ++nj) {
-            const int t = t0 + 32 * nj + lc;
-            if (t < a.L_out) {
-              // residual: C_in == C_out and L_in == L_out for the block
-              from_f32(acc[mb][nj][r] + bco + to_f32(xn[co * a.L_in + t]), &outn[co * a.L_out + t]);
-            }
+          for (int nb = 0; nb < NB; ++nb) {
+            const int t = t0 + 16 * nb + l16;
+            if (t < a.L_out)
+              from_f32(acc[mb][nb][r] + bco + to_f32(xn[co * a.L_in + t]), &outn[co * a.L_out + t]);
           }
         }
       }
@@ -269,38 +249,38 @@ conv_f32_kernel(ConvF32Args a) {
     const int cnt = min(TT, a.L_out - t0);
     const float inv_cnt = 1.f / (float)cnt;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int co = co_base + 32 * mb + 8 * (r >> 2) + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int co = co_base + 16 * mb + r;
         const bool cok = co < a.C_out;
         const float bco = (cok && a.bias) ? a.bias[co] : 0.f;
-        float y[NJ];
+        float y[NB];
         float s = 0.f;
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-          y[nj] = acc[mb][nj][r] + bco;
-          s += (t0 + 32 * nj + lc < a.L_out) ? y[nj] : 0.f;
+        for (int nb = 0; nb < NB; ++nb) {
+          y[nb] = acc[mb][nb][r] + bco;
+          s += (t0 + 16 * nb + l16 < a.L_out) ? y[nb] : 0.f;
         }
-        s = halfwave_sum(s);
+        s = quarterwave_sum(s);
         const float mean = s * inv_cnt;
         float m2 = 0.f;
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-          const float dv = y[nj] - mean;
-          m2 += (t0 + 32 * nj + lc < a.L_out) ? dv * dv : 0.f;
+        for (int nb = 0; nb < NB; ++nb) {
+          const float dv = y[nb] - mean;
+          m2 += (t0 + 16 * nb + l16 < a.L_out) ? dv * dv : 0.f;
         }
-        m2 = halfwave_sum(m2);
+        m2 = quarterwave_sum(m2);
         if (cok) {
-          if (lc == 0) {
+          if (l16 == 0) {
             float* p = a.partials + (((size_t)n * a.C_out + co) * a.n_tt + tt) * 2;
             p[0] = s;
             p[1] = m2;
           }
 #pragma unroll
-          for (int nj = 0; nj < NJ; ++nj) {
-            const int t = t0 + 32 * nj + lc;
-            if (t < a.L_out) from_f32(y[nj], &outn[co * a.L_out + t]);
+          for (int nb = 0; nb < NB; ++nb) {
+            const int t = t0 + 16 * nb + l16;
+            if (t < a.L_out) from_f32(y[nb], &outn[co * a.L_out + t]);
           }
         }
       }
@@ -341,3 +321,4 @@ hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, bool 
 }
 
 }  // namespace dconv1d
+

@@ -24,7 +24,7 @@ struct ConvF32Args {
   float* partials;       // GroupNorm: [N][C_out][n_tt][2] (tile sum, centred sum of squares)
   int N, C_in, C_out, L_in, L_out;
   int pad, dil;          // tap k reads input t - pad + k*dil
-  int NCB;               // 32-channel output blocks in the repacked weights (Cout_pad/32)
+  int NCB;               // 16-channel output blocks in the repacked weights (Cout_pad/16)
   int Q;                 // number of K-chunks = 3 * Cin_pad / KC
   int n_tt, n_ct;        // time tiles, output-channel tiles
 };

@@ -10,14 +10,14 @@
 // 2. Weight repack from PyTorch's [C_out][C_in][3] into the register order of the MFMA
 //    A operand (the first page's design turn proposes a transposed weight layout so the
 //    output-channel loop is contiguous; this goes one step further, to lane order).
-//    Index, in 16-byte units:   ((q*4 + g)*NCB + cb)*64 + lane
-//      q    = 3*c + k     K-chunk: input-channel block c (32 channels), tap k
-//      g    = 0..3        group of 8 rows inside the chunk
-//      cb   = 0..NCB-1    block of 32 output channels
-//      lane = 0..63       co = 32*cb + lane%32, rows 8g + 4*(lane/32) + u, u = 0..3
+//    Index, in 16-byte units:   (G*NCB + cb)*64 + lane
+//      G    = 2*q + g     16-row group g (0, 1) of K-chunk q = 3*c + k
+//                         (input-channel block c of 32 channels, tap k)
+//      cb   = 0..NCB-1    block of 16 output channels
+//      lane = 0..63       co = 16*cb + lane%16, rows 16g + 4*(lane/16) + u, u = 0..3
 //    and the 4 floats of the unit are u = 0..3:
-//      Wp[unit][u] = W[co][32c + 8g + 4*(lane/32) + u][k]   (0 outside C_out x C_in).
-//    A wave of the conv kernel then loads 1 KB contiguous per (q, g, cb) and each lane
+//      Wp[unit][u] = W[co][32c + 16g + 4*(lane/16) + u][k]   (0 outside C_out x C_in).
+//    A wave of the conv kernel then loads 1 KB contiguous per (G, cb) and each lane
 //    holds its A values for four consecutive MFMA steps.
 
 #include "internal.h"
@@ -36,13 +36,12 @@ prep_f32_kernel(const float* __restrict__ W, int C_out, int C_in, int NCB, int t
   if (idx < total4) {
     const int lane = idx & 63;
     int rest = idx >> 6;
-    const int cb = rest % NCB;
-    rest /= NCB;
-    const int g = rest & 3;
-    const int q = rest >> 2;
+    const int cb = rest % NCB;          // 16-channel block
+    const int G = rest / NCB;           // 16-row group: chunk G/2, half G%2
+    const int q = G >> 1, g = G & 1;
     const int c = q / 3, k = q - 3 * c;
-    const int co = 32 * cb + (lane & 31);
-    const int ci0 = 32 * c + 8 * g + 4 * (lane >> 5);
+    const int co = 16 * cb + (lane & 15);
+    const int ci0 = 32 * c + 16 * g + 4 * (lane >> 4);
     f32x4 v;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -67,7 +66,7 @@ hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, in
                            float* Wp, const float* running_mean, const float* running_var,
                            const float* gamma, const float* beta, float eps, float* scale,
                            float* shift, hipStream_t stream) {
-  const int NCB = Cout_pad / 32;
+  const int NCB = Cout_pad / 16;
   const long long total4 = 3LL * Cin_pad * Cout_pad / 4;
   const long long threads = total4 > Cin_pad ? total4 : Cin_pad;
   const int blocks = (int)((threads + 255) / 256);
