@@ -10,7 +10,6 @@ all inputs resident in HBM. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -22,16 +21,6 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv_f32_prenorm_N32_C256_L4096_d128.json")
-KERNEL_SOURCES = ["normalisation_dilated_conv1d_amd/csrc/conv_f32.hip",
-                  "normalisation_dilated_conv1d_amd/csrc/internal.h"]
-
-
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
 
 
 def measured_traffic():
@@ -42,7 +31,9 @@ def measured_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != kernel_source_digest():
+    from normalisation_dilated_conv1d_amd.profiling import source_digest
+
+    if t.get("source_sha256") != source_digest("conv_f32_kernel"):
         return None
     return t.get("traffic_bytes_per_launch")
 

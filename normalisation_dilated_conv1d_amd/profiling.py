@@ -1,0 +1,134 @@
+"""Summaries of rocprofv3 output for the library's kernels.
+
+    python -m normalisation_dilated_conv1d_amd.profiling stats KERNEL_STATS_CSV --cmd "..."
+        Markdown table of per-kernel call counts and durations from a
+        ``rocprofv3 --kernel-trace --stats --output-format csv`` run.
+
+    python -m normalisation_dilated_conv1d_amd.profiling traffic \\
+        --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel conv_f32_kernel \\
+        --calib-mib 192 --out profiles/traffic_....json --cmd-fetch "..." --cmd-write "..."
+        HBM-side bytes per launch of one kernel from two ``rocprofv3 --pmc FETCH_SIZE`` /
+        ``--pmc WRITE_SIZE`` runs. Both counters are scaled by what they read for a plain
+        device-to-device copy of --calib-mib MiB in the same run (expected: that many MiB
+        read and written), and the record carries the SHA-256 of the kernel's sources so a
+        reader can tell when it no longer describes the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = {
+    "conv_f32_kernel": ["normalisation_dilated_conv1d_amd/csrc/conv_f32.hip",
+                        "normalisation_dilated_conv1d_amd/csrc/internal.h"],
+}
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def stats_markdown(path: str, cmd: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | total (us) | average (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+        calls = int(float(r.get("Calls", 0)))
+        to_us = 1e-3  # rocprofv3 stats are in nanoseconds
+        tot = float(r.get("TotalDurationNs", 0)) * to_us
+        avg = float(r.get("AverageNs", 0)) * to_us
+        mn = float(r.get("MinNs", 0)) * to_us
+        mx = float(r.get("MaxNs", 0)) * to_us
+        pct = float(r.get("Percentage", 0))
+        out.append(f"| `{name[:90]}` | {calls} | {tot:.1f} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f}% |")
+    return "Command:\n\n```\n" + cmd + "\n```\n\n" + "\n".join(out) + "\n"
+
+
+def _per_dispatch(rows, counter):
+    d = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    return d
+
+
+def traffic_record(fetch_csv, write_csv, kernel, calib_mib, cmd_fetch, cmd_write):
+    fetch = _per_dispatch(_counter_rows(fetch_csv), "FETCH_SIZE")
+    write = _per_dispatch(_counter_rows(write_csv), "WRITE_SIZE")
+    calib_kib = calib_mib * 1024.0
+
+    def calib(vals):
+        # the copy is the copy-kernel dispatch whose reading is closest to calib_kib
+        cands = [v for (did, name), v in vals.items() if "copyBuffer" in name or "copy" in name.lower()]
+        if not cands:
+            raise SystemExit("no copy-kernel dispatch found for calibration")
+        return min(cands, key=lambda v: abs(v - calib_kib))
+
+    f_cal, w_cal = calib(fetch), calib(write)
+    f_fac, w_fac = calib_kib / f_cal, calib_kib / w_cal
+    fk = [v for (did, name), v in fetch.items() if kernel in name]
+    wk = [v for (did, name), v in write.items() if kernel in name]
+    if not fk or not wk:
+        raise SystemExit(f"kernel {kernel} not found in counter output")
+    fetch_b = statistics.median(fk) * 1024.0 * f_fac
+    write_b = statistics.median(wk) * 1024.0 * w_fac
+    return {
+        "kernel": kernel,
+        "source_sha256": source_digest(kernel),
+        "fetch_kib_per_launch_raw": statistics.median(fk),
+        "write_kib_per_launch_raw": statistics.median(wk),
+        "launches": [len(fk), len(wk)],
+        "calibration": {"copy_mib": calib_mib, "fetch_kib_read": f_cal, "write_kib_read": w_cal,
+                        "fetch_factor": f_fac, "write_factor": w_fac},
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "traffic_bytes_per_launch": fetch_b + write_b,
+        "commands": {"fetch": cmd_fetch, "write": cmd_write},
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--calib-mib", type=float, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    a = ap.parse_args(argv)
+    if a.what == "stats":
+        sys.stdout.write(stats_markdown(a.csv, a.cmd))
+    else:
+        rec = traffic_record(a.fetch, a.write, a.kernel, a.calib_mib, a.cmd_fetch, a.cmd_write)
+        with open(a.out, "w") as f:
+            json.dump(rec, f, indent=2)
+            f.write("\n")
+        print(json.dumps(rec, indent=2))
+
+
+if __name__ == "__main__":
+    main()
