@@ -6,6 +6,10 @@ workload: the BN fold + weight repack kernel and the fused implicit-GEMM kernel,
 all inputs resident in HBM. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--workload 1|3|4]
+
+--workload 3 (Conv1d+GroupNorm) and 4 (bf16 storage) time the other workloads the same
+way; the default, workload 1, is the reported metric.
 """
 from __future__ import annotations
 
@@ -19,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv_f32_prenorm_N32_C256_L4096_d128.json")
 
@@ -73,6 +78,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--workload", type=int, default=1, choices=(1, 3, 4),
+                    help="1: fp32 block N32 C256 L4096 d128 (default, the reported metric); "
+                         "3: Conv1d+GroupNorm N16 Cin128 Cout256 T1024 G32; "
+                         "4: bf16-storage block N16 C512 L16384 d128")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -84,20 +93,53 @@ def main():
     import torch
 
     import normalisation_dilated_conv1d_amd as dc
-    from normalisation_dilated_conv1d_amd.inputs import WORKLOADS, prenorm_inputs, seed_for
+    from normalisation_dilated_conv1d_amd.inputs import (WORKLOADS, groupnorm_inputs,
+                                                          prenorm_inputs, seed_for)
 
-    wl = WORKLOADS[1]
+    wl = WORKLOADS[args.workload]
     w = wl.dims
-    N, C, L, d = w["N"], w["C"], w["L"], w["d"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    p = prenorm_inputs(N, C, L, seed_for(1))
-    q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
-    out = torch.empty_like(q["x"])
+    if wl.kind == "prenorm":
+        N, C, L, d = w["N"], w["C"], w["L"], w["d"]
+        bf16 = w["dtype"] == "bf16"
+        p = prenorm_inputs(N, C, L, seed_for(args.workload), bf16=bf16)
+        q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+        out = torch.empty_like(q["x"])
+        fn = dc.prenorm_dconv1d_fwd_bf16 if bf16 else dc.prenorm_dconv1d_fwd
 
-    def step():
-        dc.prenorm_dconv1d_fwd(q["x"], q["running_mean"], q["running_var"], q["gamma"],
-                               q["beta"], q["eps"], q["W"], q["b"], d, out=out)
+        def step():
+            fn(q["x"], q["running_mean"], q["running_var"], q["gamma"], q["beta"], q["eps"],
+               q["W"], q["b"], d, out=out)
+
+        C_in = C_out = C
+        T_out = L
+        esz = 2 if bf16 else 4
+        flops = 2.0 * N * L * C * 3 * C
+        alg_bytes = esz * 2.0 * N * C * L + 4.0 * (3 * C * C + 5 * C)
+        config = {"workload": wl.name, "N": N, "C": C, "L": L, "kernel_size": 3,
+                  "dilation": d, "padding": d, "parallelism": "single GPU"}
+        kernel_name = ("conv_bf16_kernel<pair>" if bf16
+                       else "conv_f32_kernel<128, BN, residual, float>")
+    else:
+        N, C_in, C_out, T, G = w["N"], w["C_in"], w["C_out"], w["T"], w["G"]
+        p = groupnorm_inputs(N, C_in, C_out, T, seed_for(args.workload))
+        q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+        T_out = T + 2 * w["padding"] - 2 * w["dilation"]
+        out = torch.empty((N, C_out, T_out), device=dev)
+        bf16 = False
+
+        def step():
+            dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"],
+                                    G, w["padding"], w["dilation"], out=out)
+
+        flops = 2.0 * N * T_out * C_out * 3 * C_in
+        # x once, y written and read back, out written, W and the affine vectors
+        alg_bytes = 4.0 * (N * C_in * T + 3 * N * C_out * T_out + 3 * C_in * C_out + 2 * C_out)
+        config = {"workload": wl.name, "N": N, "C_in": C_in, "C_out": C_out, "T": T,
+                  "num_groups": G, "kernel_size": 3, "padding": w["padding"],
+                  "dilation": w["dilation"], "parallelism": "single GPU"}
+        kernel_name = "conv_f32_kernel<64, no BN, GroupNorm statistics, float>"
 
     for _ in range(args.warmup):
         step()
@@ -130,14 +172,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    flops = 2.0 * N * L * C * 3 * C
-    alg_bytes = 4.0 * (2 * N * C * L + 3 * C * C + 5 * C)
+    peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
     k_tflops = flops / (kern_ms_avg * 1e-3) / 1e12
+    metric = ("fused block TFLOP/s & GB/s (N32 C256 L4096 d128) vs MI355X roofline"
+              if args.workload == 1 else f"TFLOP/s & GB/s, {wl.name}, vs MI355X roofline")
 
     line = {
-        "metric": "fused block TFLOP/s & GB/s (N32 C256 L4096 d128) vs MI355X roofline",
+        "metric": metric,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -147,22 +190,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "N": N, "C": C, "L": L, "kernel_size": 3,
-                   "dilation": d, "padding": d, "parallelism": "single GPU"},
+        "config": config,
         "hbm_gbps_algorithmic": round(gbps, 2),
-        "frac_fp32_mfma_peak": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(k_tflops, 3),
-                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "conv_f32_kernel<128, BN, residual, float>",
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(k_tflops / peak, 4),
+                     "traffic": measured_traffic() if args.workload == 1 else None,
+                     "kernel": kernel_name,
                      "kernel_ms": round(kern_ms_avg, 5),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": alg_bytes},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == 1:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

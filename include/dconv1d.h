@@ -93,9 +93,9 @@ int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* 
  *
  * x and out are bfloat16 bit patterns (uint16_t, [N][C][L]); every other argument is
  * as in prenorm_dconv1d_fwd (float32 parameters, W in float32 PyTorch layout). BN and
- * ReLU run in float32 on the bfloat16 x, the contraction runs on float32 MFMA with
- * float32 accumulation, bias and the bfloat16 residual are added in float32, and out is
- * rounded to bfloat16 (round to nearest even).
+ * ReLU run in float32 on the bfloat16 x; the activation and W are rounded to bfloat16
+ * (round to nearest even) for the bf16 MFMA, products accumulate in float32, bias and
+ * the bfloat16 residual are added in float32, and out is rounded to bfloat16 (RNE).
  */
 int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
                              const float* running_var, const float* gamma, const float* beta,

@@ -149,10 +149,13 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   if (overlaps(x, bytes, out, bytes)) return fail(DCONV1D_EALIAS, "out overlaps x");
 
   const int Ci = (int)C, Li = (int)L;
-  const int Cin_pad = round_up(Ci, KC);
+  // bf16 storage runs the bf16-MFMA kernel: 64-channel K-chunks, 128-step time tiles
+  const int Cin_pad = round_up(Ci, bf16 ? KC_BF16 : KC);
   const int Cout_pad = round_up(Ci, CO_TILE_F32);
   const int n_ct = Cout_pad / CO_TILE_F32;
-  const int tile_t = conv_f32_tile_t(EPI_RESIDUAL, Li, (int)std::min<int64_t>(N * n_ct, kMaxIndex));
+  const int tile_t = bf16 ? TILE_T_BF16
+                          : conv_f32_tile_t(EPI_RESIDUAL, Li,
+                                            (int)std::min<int64_t>(N * n_ct, kMaxIndex));
   const int n_tt = (Li + tile_t - 1) / tile_t;
   if (N * n_tt * n_ct > kMaxIndex)
     return fail(DCONV1D_EINVAL, "grid of %lld workgroups is too large",
@@ -163,26 +166,30 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   // keeps every tap offset inside int range.
   const int d_eff = (int)std::min<int64_t>(d, L);
 
+  const size_t wp_bytes = (bf16 ? 2 : 4) * 3 * (size_t)Cin_pad * Cout_pad;
   const size_t off_scale = 0;
   const size_t off_shift = align256(off_scale + sizeof(float) * Cin_pad);
   const size_t off_wp = align256(off_shift + sizeof(float) * Cin_pad);
-  const size_t total = align256(off_wp + sizeof(float) * 3 * (size_t)Cin_pad * Cout_pad);
+  const size_t total = align256(off_wp + wp_bytes);
   char* ws = nullptr;
   st = get_workspace(total, &ws);
   if (st != DCONV1D_OK) return st;
   float* scale = reinterpret_cast<float*>(ws + off_scale);
   float* shift = reinterpret_cast<float*>(ws + off_shift);
-  float* Wp = reinterpret_cast<float*>(ws + off_wp);
+  void* Wp = ws + off_wp;
 
-  hipError_t e = launch_prep_f32(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var,
-                                 gamma, beta, eps, scale, shift, stream);
+  hipError_t e =
+      bf16 ? launch_prep_bf16(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var, gamma,
+                              beta, eps, scale, shift, stream)
+           : launch_prep_f32(W, Ci, Ci, Cout_pad, Cin_pad, static_cast<float*>(Wp), running_mean,
+                             running_var, gamma, beta, eps, scale, shift, stream);
   if (e != hipSuccess) return hip_fail(e, "prep kernel launch");
 
   ConvF32Args a{};
   a.x = x;
   a.scale = scale;
   a.shift = shift;
-  a.Wp = Wp;
+  a.Wp = static_cast<const float*>(Wp);
   a.bias = b;
   a.out = out;
   a.partials = nullptr;
@@ -194,11 +201,11 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   a.pad = d_eff;
   a.dil = d_eff;
   a.NCB = Cout_pad / 16;
-  a.Q = 3 * Cin_pad / KC;
+  a.Q = 3 * Cin_pad / (bf16 ? KC_BF16 : KC);
   a.n_tt = n_tt;
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
-  e = launch_conv_f32(a, tile_t, EPI_RESIDUAL, bf16, stream);
+  e = bf16 ? launch_conv_bf16(a, stream) : launch_conv_f32(a, tile_t, EPI_RESIDUAL, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
   return DCONV1D_OK;
@@ -300,7 +307,7 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
   a.n_tt = n_tt;
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
-  e = launch_conv_f32(a, tile_t, EPI_GN_STATS, false, stream);
+  e = launch_conv_f32(a, tile_t, EPI_GN_STATS, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
   e = launch_gn_normalize(out, part, gamma, beta, eps, (int)N, (int)C_out, Lo, (int)num_groups,

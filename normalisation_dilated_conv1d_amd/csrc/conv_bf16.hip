@@ -1,0 +1,328 @@
+// bfloat16 implicit-GEMM kernel for the pre-norm residual block with bfloat16 storage of
+// x and out (POPCORNBENCH "Kimi-K2.6__l2_p12", first turn: block definition, eval-mode
+// BN per channel, zero padding of the conv input, residual add).
+//
+// Same GEMM view and work split as the float32 kernel (conv_f32.hip): one workgroup per
+// (sample, 256 output channels, 128 time steps), 4 waves of 64 channels x 128 steps,
+// activations through LDS, weights straight from global memory into registers. What
+// changes for bfloat16:
+//
+//   MFMA       = v_mfma_f32_16x16x32_bf16: 16x16 output block, K = 32 per instruction,
+//                float32 accumulation. A lane feeds 8 consecutive K values of one row
+//                (A) and of one column (B), so both operands must be K-contiguous.
+//   K loop     = chunks of 64 input channels of one tap (two MFMA K-steps), ordered
+//                (channel block, tap).
+//   B operand  = the chunk's activations z = ReLU(BN(x)) rounded to bfloat16, staged
+//                transposed in LDS as [time column][64 channel rows], so the 8 rows a lane
+//                needs are 16 contiguous bytes: one ds_read_b128 per MFMA. Each staging
+//                lane holds 8 consecutive rows of a column in registers and writes them
+//                with one ds_write_b128.
+//   A operand  = weights rounded to bfloat16 by the repack kernel and stored in lane
+//                order: one 16-byte load per (K-step, 16-channel block) per lane, loaded
+//                one K-step ahead through a 2-slot register ring.
+//   x loads    = when every tap offset and L are even, each lane loads two adjacent time
+//                steps with one aligned 4-byte load; otherwise two 2-byte loads.
+//
+// K-slot mapping: in K-step s of a chunk, quarter-wave q = lane/16 element e (0..7) is
+// chunk row 32s + 8q + e, for A and B alike, so the sum over K is the plain sum over
+// (channel, tap).
+
+#include "internal.h"
+
+namespace dconv1d {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace
+
+constexpr int KCB = KC_BF16;    // channel rows per chunk
+constexpr int TTB = TILE_T_BF16;   // time steps per workgroup
+
+template <bool PAIR>
+__global__ void __launch_bounds__(NTHREADS, 2)
+conv_bf16_kernel(ConvF32Args a) {
+  constexpr int NB = TTB / 16;              // 16-column MFMA blocks per wave (8)
+  constexpr int RPW = KCB / 4;              // staged rows per wave (16)
+  constexpr int PITCH = KCB + 8;            // bf16 per LDS column (144 bytes)
+  __shared__ __attribute__((aligned(16))) uint16_t zs[2][TTB * PITCH];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int lq = l >> 4;
+  const int l16 = l & 15;
+
+  const int nwg = gridDim.x;
+  const int b = blockIdx.x;
+  const int per = nwg >> 3, rem = nwg & 7, xcd = b & 7;
+  const int logical = xcd * per + min(xcd, rem) + (b >> 3);
+  const int ct = logical % a.n_ct;
+  const int rest = logical / a.n_ct;
+  const int tt = rest % a.n_tt;
+  const int n = rest / a.n_tt;
+  const int t0 = tt * TTB;
+
+  const uint16_t* __restrict__ xn =
+      reinterpret_cast<const uint16_t*>(a.x) + (size_t)n * a.C_in * a.L_in;
+  const u32x4* __restrict__ Wp4 = reinterpret_cast<const u32x4*>(a.Wp);
+  const int cb0 = (ct * CO_TILE_F32) / 16 + 4 * w;
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mb][nb][r] = 0.f;
+
+  // Staging: wave w stages rows [16w, 16w + 16) of the chunk. PAIR: lane l covers columns
+  // 2l and 2l+1 with one 4-byte load per row; otherwise columns l and l + 64, 2 bytes each.
+  uint32_t xr[RPW * (PAIR ? 1 : 2)];
+  float sc[RPW], sh[RPW];
+
+  auto load_x = [&](int q) {
+    const int c = q / 3, k = q - 3 * c;
+    const int off = k * a.dil - a.pad;
+    if (PAIR) {
+      const int ts = t0 + 2 * l + off;
+      const int tsc = min(max(ts, 0), a.L_in - 2);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
+        xr[i] = *reinterpret_cast<const uint32_t*>(xn + (size_t)ci * a.L_in + tsc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ts = t0 + l + 64 * j + off;
+        const int tsc = min(max(ts, 0), a.L_in - 1);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
+          xr[j * RPW + i] = xn[(size_t)ci * a.L_in + tsc];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      sc[i] = a.scale[c * KCB + RPW * w + i];
+      sh[i] = a.shift[c * KCB + RPW * w + i];
+    }
+  };
+  // z = ReLU(scale*x + shift) in float32, exactly 0 in the padding, rounded to bf16;
+  // 8 consecutive rows of one column go to LDS with one 16-byte write. `get(i)` returns
+  // row i of the column as float, converted straight from the loaded bits.
+  auto stage_column = [&](auto&& get, int col, uint32_t tkeep, int c, uint16_t* dst) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int i0 = 8 * half + e, i1 = i0 + 1;
+        const uint32_t k0 = (c * KCB + RPW * w + i0 < a.C_in) ? tkeep : 0u;
+        const uint32_t k1 = (c * KCB + RPW * w + i1 < a.C_in) ? tkeep : 0u;
+        const float z0 = __uint_as_float(__float_as_uint(fmaxf(fmaf(get(i0), sc[i0], sh[i0]), 0.f)) & k0);
+        const float z1 = __uint_as_float(__float_as_uint(fmaxf(fmaf(get(i1), sc[i1], sh[i1]), 0.f)) & k1);
+        packed[e >> 1] = f32_to_bf16(z0) | (f32_to_bf16(z1) << 16);
+      }
+      u32x4 pv = {packed[0], packed[1], packed[2], packed[3]};
+      *reinterpret_cast<u32x4*>(dst + col * PITCH + RPW * w + 8 * half) = pv;
+    }
+  };
+  auto store_z = [&](int q, uint16_t* dst) {
+    const int c = q / 3, k = q - 3 * c;
+    const int off = k * a.dil - a.pad;
+    if (PAIR) {
+      const int ts = t0 + 2 * l + off;
+      // with even offsets and even L both time steps of the pair are in or out together
+      uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
+      asm volatile("" : "+v"(tkeep));
+      stage_column([&](int i) { return bf16_lo(xr[i]); }, 2 * l, tkeep, c, dst);
+      stage_column([&](int i) { return bf16_hi(xr[i]); }, 2 * l + 1, tkeep, c, dst);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = l + 64 * j;
+        const int ts = t0 + col + off;
+        uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
+        asm volatile("" : "+v"(tkeep));
+        stage_column([&](int i) { return bf16_to_f32((uint16_t)xr[j * RPW + i]); }, col, tkeep,
+                     c, dst);
+      }
+    }
+  };
+  // A operands of global K-step S (chunk S/2, step S%2): one 16-byte unit per
+  // 16-channel block. Clamped to the last step so prefetches past the end stay in bounds.
+  const int n_steps = 2 * a.Q;
+  auto load_w = [&](int S, u32x4 (&dst)[4]) {
+    S = min(S, n_steps - 1);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) dst[mb] = Wp4[(S * a.NCB + cb0 + mb) * 64 + l];
+  };
+  auto load_b = [&](const uint16_t* zb, int s, int nb) -> bf16x8 {
+    const u32x4 v =
+        *reinterpret_cast<const u32x4*>(zb + (16 * nb + l16) * PITCH + 32 * s + 8 * lq);
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  u32x4 wr[2][4];   // ring of 2 K-steps x 4 channel blocks; slot = K-step parity
+
+  // One chunk (two K-steps) on LDS buffer zb; `mid` stages the next chunk between them.
+  // The weights of K-step S + 1 are loaded while K-step S runs.
+  auto compute = [&](const uint16_t* zb, int q, auto&& mid) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int S = 2 * q + s;
+      load_w(S + 1, wr[(s + 1) & 1]);
+      bf16x8 bv[2];
+      bv[0] = load_b(zb, s, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (nb + 1 < NB) bv[(nb + 1) & 1] = load_b(zb, s, nb + 1);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, wr[s][mb]), bv[nb & 1],
+              acc[mb][nb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // One chunk per trip; the LDS buffer alternates with the chunk's parity. The staged
+  // chunk index is clamped to the last chunk, so the body has no branches; the last trip
+  // stages that chunk a second time into the idle buffer.
+  const int Q = a.Q;
+  load_w(0, wr[0]);
+  load_x(0);
+  store_z(0, zs[0]);
+  __syncthreads();
+  for (int q = 0; q < Q; ++q) {
+    const int qn = min(q + 1, Q - 1);
+    load_x(qn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(zs[q & 1], q, [&] { store_z(qn, zs[(q + 1) & 1]); });
+    __syncthreads();
+  }
+
+  // Epilogue: register r of block (mb, nb) is channel 16mb + 4*lq + r, time 16nb + l16.
+  uint16_t* __restrict__ outn = reinterpret_cast<uint16_t*>(a.out) + (size_t)n * a.C_out * a.L_out;
+  const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
+  // One 16-channel block at a time, so at most 32 residual loads are in flight.
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int co = co_base + 16 * mb + r;
+      if (co < a.C_out) {
+        const float bco = a.bias ? a.bias[co] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int t = t0 + 16 * nb + l16;
+          if (t < a.L_out) {
+            const float o = acc[mb][nb][r] + bco + bf16_to_f32(xn[(size_t)co * a.L_in + t]);
+            outn[(size_t)co * a.L_out + t] = (uint16_t)f32_to_bf16(o);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Per-call preparation for the bf16 kernel, one launch: the BN fold (as in prep.hip:
+// scale = gamma/sqrt(var+eps), shift = beta - mean*scale, in double, rounded once) and
+// the weight repack W[C_out][C_in][3] float32 -> bfloat16 (round to nearest even) in
+// A-operand lane order. Unit (16 bytes) index (S*NCB + cb)*64 + lane, with S = 2*q + s
+// the global K-step (chunk q = 3*c + k: channel block c of 64, tap k) and cb the
+// 16-channel block; element e of the unit is
+//   W[16*cb + lane%16][64*c + 32*s + 8*(lane/16) + e][k]   (0 outside C_out x C_in).
+__global__ void __launch_bounds__(256)
+prep_bf16_kernel(const float* __restrict__ W, int C_out, int C_in, int NCB, int total,
+                 u32x4* __restrict__ Wp, const float* __restrict__ mean,
+                 const float* __restrict__ var, const float* __restrict__ gamma,
+                 const float* __restrict__ beta, float eps, float* __restrict__ scale,
+                 float* __restrict__ shift, int Cin_pad) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < total) {
+    const int lane = idx & 63;
+    const int rest = idx >> 6;
+    const int cb = rest % NCB;
+    const int S = rest / NCB;
+    const int q = S >> 1, s = S & 1;
+    const int c = q / 3, k = q - 3 * c;
+    const int co = 16 * cb + (lane & 15);
+    const int ci0 = KCB * c + 32 * s + 8 * (lane >> 4);
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ci = ci0 + e;
+      const float v = (co < C_out && ci < C_in) ? W[((size_t)co * C_in + ci) * 3 + k] : 0.f;
+      h[e] = f32_to_bf16(v);
+    }
+    u32x4 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+               h[6] | (h[7] << 16)};
+    Wp[idx] = o;
+  }
+  if (idx < Cin_pad) {
+    float sc = 0.f, sh = 0.f;
+    if (idx < C_in) {
+      const double sd = (double)gamma[idx] / sqrt((double)var[idx] + (double)eps);
+      sc = (float)sd;
+      sh = (float)((double)beta[idx] - (double)mean[idx] * sd);
+    }
+    scale[idx] = sc;
+    shift[idx] = sh;
+  }
+}
+
+hipError_t launch_prep_bf16(const float* W, int C_out, int C_in, int Cout_pad, int Cin_pad,
+                            void* Wp, const float* running_mean, const float* running_var,
+                            const float* gamma, const float* beta, float eps, float* scale,
+                            float* shift, hipStream_t stream) {
+  const int NCB = Cout_pad / 16;
+  const long long total = 3LL * Cin_pad * Cout_pad / 8;   // 16-byte units of 8 bf16
+  const long long threads = total > Cin_pad ? total : Cin_pad;
+  const int blocks = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL(prep_bf16_kernel, dim3(blocks), dim3(256), 0, stream, W, C_out, C_in, NCB,
+                     (int)total, reinterpret_cast<u32x4*>(Wp), running_mean, running_var, gamma,
+                     beta, eps, scale, shift, Cin_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_bf16(const ConvF32Args& a, hipStream_t stream) {
+  const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // every tap offset and tile start is even, L is even and x is 4-byte aligned: each
+  // lane can load an aligned pair of time steps
+  const bool pair = ((a.dil | a.pad | a.L_in) & 1) == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.x) & 3) == 0;
+  if (pair)
+    hipLaunchKernelGGL(conv_bf16_kernel<true>, dim3((unsigned)nwg), dim3(NTHREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(conv_bf16_kernel<false>, dim3((unsigned)nwg), dim3(NTHREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dconv1d

@@ -64,18 +64,9 @@ __device__ __forceinline__ float quarterwave_sum(float v) {
   return v;
 }
 
-// Storage conversions. bfloat16 is carried as its 16-bit pattern; widening is exact,
-// narrowing rounds to nearest even (NaN stays a quiet NaN).
+// Storage type hooks (the kernel is instantiated for float storage).
 __device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ __forceinline__ void from_f32(float v, float* dst) { *dst = v; }
-__device__ __forceinline__ void from_f32(float v, uint16_t* dst) {
-  const uint32_t u = __float_as_uint(v);
-  uint16_t r;
-  if ((u & 0x7fffffffu) > 0x7f800000u) r = (uint16_t)((u >> 16) | 0x40u);
-  else r = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-  *dst = r;
-}
 
 template <int TT, bool BN, int EPI, typename XT>
 __global__ void __launch_bounds__(NTHREADS, 2)
@@ -301,21 +292,17 @@ static hipError_t launch_one(const ConvF32Args& a, int nwg, hipStream_t stream) 
   return hipGetLastError();
 }
 
-hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, bool bf16_storage,
-                           hipStream_t stream) {
+hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, hipStream_t stream) {
   const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const bool bn = a.scale != nullptr;
   if (epilogue == EPI_RESIDUAL) {
     if (!bn) return hipErrorInvalidValue;
-    if (bf16_storage)
-      return tile_t == 128 ? launch_one<128, true, EPI_RESIDUAL, uint16_t>(a, (int)nwg, stream)
-                           : launch_one<64, true, EPI_RESIDUAL, uint16_t>(a, (int)nwg, stream);
     return tile_t == 128 ? launch_one<128, true, EPI_RESIDUAL, float>(a, (int)nwg, stream)
                          : launch_one<64, true, EPI_RESIDUAL, float>(a, (int)nwg, stream);
   }
-  if (bn || bf16_storage) return hipErrorInvalidValue;
+  if (bn) return hipErrorInvalidValue;
   return tile_t == 128 ? launch_one<128, false, EPI_GN_STATS, float>(a, (int)nwg, stream)
                        : launch_one<64, false, EPI_GN_STATS, float>(a, (int)nwg, stream);
 }

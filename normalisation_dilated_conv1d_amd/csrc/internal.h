@@ -15,7 +15,7 @@ constexpr int NTHREADS = 256;
 // Arguments of the float32 implicit-GEMM conv kernel. Sizes are int: the host checks
 // that every per-sample index (C*L) fits in 31 bits; the sample offset is 64-bit.
 struct ConvF32Args {
-  const void* x;         // [N][C_in][L_in], float32 or bfloat16 bits
+  const void* x;         // [N][C_in][L_in], float32 (bfloat16 bits for the bf16 kernel)
   const float* scale;    // [Cin_pad] folded BN scale (nullptr: no BN/ReLU on load)
   const float* shift;    // [Cin_pad] folded BN shift
   const float* Wp;       // repacked weights, see prep.hip
@@ -41,8 +41,16 @@ hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, in
 
 // conv_f32.hip
 int conv_f32_tile_t(int epilogue, int L_out, int tiles_other);
-hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, bool bf16_storage,
-                           hipStream_t stream);
+hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, hipStream_t stream);
+
+// conv_bf16.hip: input channels padded to a multiple of 64, 128 time steps per tile
+constexpr int KC_BF16 = 64;
+constexpr int TILE_T_BF16 = 128;
+hipError_t launch_prep_bf16(const float* W, int C_out, int C_in, int Cout_pad, int Cin_pad,
+                            void* Wp, const float* running_mean, const float* running_var,
+                            const float* gamma, const float* beta, float eps, float* scale,
+                            float* shift, hipStream_t stream);
+hipError_t launch_conv_bf16(const ConvF32Args& a, hipStream_t stream);
 
 // gn.hip
 hipError_t launch_gn_normalize(float* out, const float* partials, const float* gamma,
