@@ -150,7 +150,7 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
 
   const int Ci = (int)C, Li = (int)L;
   // bf16 storage runs the bf16-MFMA kernel: 64-channel K-chunks, 128-step time tiles
-  const int Cin_pad = round_up(Ci, bf16 ? KC_BF16 : KC);
+  const int Cin_pad = round_up(Ci, bf16 ? CIN_PAD_BF16 : KC);
   const int Cout_pad = round_up(Ci, CO_TILE_F32);
   const int n_ct = Cout_pad / CO_TILE_F32;
   const int tile_t = bf16 ? TILE_T_BF16

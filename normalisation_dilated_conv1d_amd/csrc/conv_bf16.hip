@@ -11,7 +11,7 @@
 //                float32 accumulation. A lane feeds 8 consecutive K values of one row
 //                (A) and of one column (B), so both operands must be K-contiguous.
 //   K loop     = chunks of 64 input channels of one tap (two MFMA K-steps), ordered
-//                (channel block, tap).
+//                (channel block, tap); C_in is padded to 128 so the chunk count is even.
 //   B operand  = the chunk's activations z = ReLU(BN(x)) rounded to bfloat16, staged
 //                transposed in LDS as [time column][64 channel rows], so the 8 rows a lane
 //                needs are 16 contiguous bytes: one ds_read_b128 per MFMA. Each staging
@@ -19,7 +19,7 @@
 //                with one ds_write_b128.
 //   A operand  = weights rounded to bfloat16 by the repack kernel and stored in lane
 //                order: one 16-byte load per (K-step, 16-channel block) per lane, loaded
-//                one K-step ahead through a 2-slot register ring.
+//                two K-steps ahead through a 4-slot register ring.
 //   x loads    = when every tap offset and L are even, each lane loads two adjacent time
 //                steps with one aligned 4-byte load; otherwise two 2-byte loads.
 //
@@ -32,6 +32,8 @@
 namespace dconv1d {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -50,8 +52,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float v) {
 
 }  // namespace
 
-constexpr int KCB = KC_BF16;    // channel rows per chunk
-constexpr int TTB = TILE_T_BF16;   // time steps per workgroup
+template <int V>
+struct Parity {
+  static constexpr int value = V;
+};
+
+constexpr int KCB = 64;   // channel rows per chunk (two MFMA K-steps)
+constexpr int TTB = TILE_T_BF16;  // time steps per workgroup
 
 template <bool PAIR>
 __global__ void __launch_bounds__(NTHREADS, 2)
@@ -118,27 +125,33 @@ conv_bf16_kernel(ConvF32Args a) {
         }
       }
     }
+    // wave-uniform addresses: read through the constant address space so the
+    // compiler issues scalar loads into SGPRs
+    const __attribute__((address_space(4))) float* scp =
+        (const __attribute__((address_space(4))) float*)(a.scale + c * KCB + RPW * w);
+    const __attribute__((address_space(4))) float* shp =
+        (const __attribute__((address_space(4))) float*)(a.shift + c * KCB + RPW * w);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      sc[i] = a.scale[c * KCB + RPW * w + i];
-      sh[i] = a.shift[c * KCB + RPW * w + i];
+      sc[i] = scp[i];
+      sh[i] = shp[i];
     }
   };
-  // z = ReLU(scale*x + shift) in float32, exactly 0 in the padding, rounded to bf16;
-  // 8 consecutive rows of one column go to LDS with one 16-byte write. `get(i)` returns
-  // row i of the column as float, converted straight from the loaded bits.
-  auto stage_column = [&](auto&& get, int col, uint32_t tkeep, int c, uint16_t* dst) {
+  // z = ReLU(scale*x + shift) in float32, rounded to bf16 by the hardware pack (round to
+  // nearest even), exactly 0 in the time padding; 8 consecutive rows of one column go to
+  // LDS with one 16-byte write. `get(i)` returns row i of the column as float, converted
+  // straight from the loaded bits. Channels past C_in need no mask: their folded scale
+  // and shift are 0, so z = max(0*x + 0, 0) = 0 for the (finite) clamped load.
+  auto stage_column = [&](auto&& get, int col, uint32_t tkeep, uint16_t* dst) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t packed[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const int i0 = 8 * half + e, i1 = i0 + 1;
-        const uint32_t k0 = (c * KCB + RPW * w + i0 < a.C_in) ? tkeep : 0u;
-        const uint32_t k1 = (c * KCB + RPW * w + i1 < a.C_in) ? tkeep : 0u;
-        const float z0 = __uint_as_float(__float_as_uint(fmaxf(fmaf(get(i0), sc[i0], sh[i0]), 0.f)) & k0);
-        const float z1 = __uint_as_float(__float_as_uint(fmaxf(fmaf(get(i1), sc[i1], sh[i1]), 0.f)) & k1);
-        packed[e >> 1] = f32_to_bf16(z0) | (f32_to_bf16(z1) << 16);
+        const f32x2 z = {fmaxf(fmaf(get(i0), sc[i0], sh[i0]), 0.f),
+                         fmaxf(fmaf(get(i1), sc[i1], sh[i1]), 0.f)};
+        packed[e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2)) & tkeep;
       }
       u32x4 pv = {packed[0], packed[1], packed[2], packed[3]};
       *reinterpret_cast<u32x4*>(dst + col * PITCH + RPW * w + 8 * half) = pv;
@@ -152,8 +165,8 @@ conv_bf16_kernel(ConvF32Args a) {
       // with even offsets and even L both time steps of the pair are in or out together
       uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
       asm volatile("" : "+v"(tkeep));
-      stage_column([&](int i) { return bf16_lo(xr[i]); }, 2 * l, tkeep, c, dst);
-      stage_column([&](int i) { return bf16_hi(xr[i]); }, 2 * l + 1, tkeep, c, dst);
+      stage_column([&](int i) { return bf16_lo(xr[i]); }, 2 * l, tkeep, dst);
+      stage_column([&](int i) { return bf16_hi(xr[i]); }, 2 * l + 1, tkeep, dst);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -162,7 +175,7 @@ conv_bf16_kernel(ConvF32Args a) {
         uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
         asm volatile("" : "+v"(tkeep));
         stage_column([&](int i) { return bf16_to_f32((uint16_t)xr[j * RPW + i]); }, col, tkeep,
-                     c, dst);
+                     dst);
       }
     }
   };
@@ -180,15 +193,24 @@ conv_bf16_kernel(ConvF32Args a) {
     return __builtin_bit_cast(bf16x8, v);
   };
 
-  u32x4 wr[2][4];   // ring of 2 K-steps x 4 channel blocks; slot = K-step parity
+  // Weights rotate through a ring of 4 K-step slots, loaded two K-steps ahead. The chunk
+  // count is even (C_in is padded to 128), so the loop takes two chunks per trip and
+  // every slot index (2*parity + s) % 4 is a compile-time constant.
+  // (The 2-byte-load variant holds twice the staging registers, so it keeps a 2-slot
+  // ring loaded one K-step ahead.)
+  constexpr int RING = PAIR ? 4 : 2;
+  constexpr int DIST = PAIR ? 2 : 1;
+  u32x4 wr[RING][4];
 
-  // One chunk (two K-steps) on LDS buffer zb; `mid` stages the next chunk between them.
-  // The weights of K-step S + 1 are loaded while K-step S runs.
-  auto compute = [&](const uint16_t* zb, int q, auto&& mid) {
+  // One chunk (two K-steps) on LDS buffer zb. `next` stages the next chunk into the
+  // other buffer after the chunk's MFMAs, the latest point before the barrier, which
+  // gives its x loads (issued at the chunk's start) the longest time to arrive.
+  auto compute = [&](const uint16_t* zb, int q, auto P, auto&& next) {
+    constexpr int par = decltype(P)::value;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int S = 2 * q + s;
-      load_w(S + 1, wr[(s + 1) & 1]);
+      load_w(S + DIST, wr[(2 * par + s + DIST) % RING]);
       bf16x8 bv[2];
       bv[0] = load_b(zb, s, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -198,30 +220,32 @@ conv_bf16_kernel(ConvF32Args a) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, wr[s][mb]), bv[nb & 1],
+              __builtin_bit_cast(bf16x8, wr[(2 * par + s) % RING][mb]), bv[nb & 1],
               acc[mb][nb], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (s == 0) {
-        mid();
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
+    next();
   };
 
-  // One chunk per trip; the LDS buffer alternates with the chunk's parity. The staged
-  // chunk index is clamped to the last chunk, so the body has no branches; the last trip
-  // stages that chunk a second time into the idle buffer.
+  // Two chunks per trip. The staged chunk index is clamped to the last chunk, so the
+  // body has no branches; the last trip stages that chunk a second time into the idle
+  // buffer.
   const int Q = a.Q;
-  load_w(0, wr[0]);
+#pragma unroll
+  for (int S = 0; S < DIST; ++S) load_w(S, wr[S]);
   load_x(0);
   store_z(0, zs[0]);
   __syncthreads();
-  for (int q = 0; q < Q; ++q) {
-    const int qn = min(q + 1, Q - 1);
+  for (int q = 0; q < Q; q += 2) {
+    load_x(q + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(zs[0], q, Parity<0>{}, [&] { store_z(q + 1, zs[1]); });
+    __syncthreads();
+    const int qn = min(q + 2, Q - 1);
     load_x(qn);
     __builtin_amdgcn_sched_barrier(0);
-    compute(zs[q & 1], q, [&] { store_z(qn, zs[(q + 1) & 1]); });
+    compute(zs[1], q + 1, Parity<1>{}, [&] { store_z(qn, zs[0]); });
     __syncthreads();
   }
 
@@ -241,7 +265,7 @@ conv_bf16_kernel(ConvF32Args a) {
           const int t = t0 + 16 * nb + l16;
           if (t < a.L_out) {
             const float o = acc[mb][nb][r] + bco + bf16_to_f32(xn[(size_t)co * a.L_in + t]);
-            outn[(size_t)co * a.L_out + t] = (uint16_t)f32_to_bf16(o);
+            outn[(size_t)co * a.L_out + t] = __builtin_bit_cast(uint16_t, (__bf16)o);
           }
         }
       }

@@ -43,8 +43,10 @@ hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, in
 int conv_f32_tile_t(int epilogue, int L_out, int tiles_other);
 hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, hipStream_t stream);
 
-// conv_bf16.hip: input channels padded to a multiple of 64, 128 time steps per tile
+// conv_bf16.hip: 64-channel K-chunks, input channels padded to a multiple of 128 (an
+// even chunk count), 128 time steps per tile
 constexpr int KC_BF16 = 64;
+constexpr int CIN_PAD_BF16 = 128;
 constexpr int TILE_T_BF16 = 128;
 hipError_t launch_prep_bf16(const float* W, int C_out, int C_in, int Cout_pad, int Cin_pad,
                             void* Wp, const float* running_mean, const float* running_var,
