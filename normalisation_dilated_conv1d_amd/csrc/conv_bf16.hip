@@ -252,25 +252,35 @@ conv_bf16_kernel(ConvF32Args a) {
   // Epilogue: register r of block (mb, nb) is channel 16mb + 4*lq + r, time 16nb + l16.
   uint16_t* __restrict__ outn = reinterpret_cast<uint16_t*>(a.out) + (size_t)n * a.C_out * a.L_out;
   const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
-  // One 16-channel block at a time, so at most 32 residual loads are in flight.
+  // Residual and bias loads use clamped (always in-bounds) addresses and are issued a
+  // 16-channel block at a time before any use, so each block pays the memory latency
+  // once; only the stores are predicated.
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
+    uint16_t res[4][NB];
+    float bco[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int coc = min(co_base + 16 * mb + r, a.C_out - 1);
+      bco[r] = a.bias ? a.bias[coc] : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int tc = min(t0 + 16 * nb + l16, a.L_out - 1);
+        res[r][nb] = xn[(size_t)coc * a.L_in + tc];
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int co = co_base + 16 * mb + r;
-      if (co < a.C_out) {
-        const float bco = a.bias ? a.bias[co] : 0.f;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int t = t0 + 16 * nb + l16;
-          if (t < a.L_out) {
-            const float o = acc[mb][nb][r] + bco + bf16_to_f32(xn[(size_t)co * a.L_in + t]);
-            outn[(size_t)co * a.L_out + t] = __builtin_bit_cast(uint16_t, (__bf16)o);
-          }
+      for (int nb = 0; nb < NB; ++nb) {
+        const int t = t0 + 16 * nb + l16;
+        if (co < a.C_out && t < a.L_out) {
+          const float o = acc[mb][nb][r] + bco[r] + bf16_to_f32(res[r][nb]);
+          outn[(size_t)co * a.L_out + t] = __builtin_bit_cast(uint16_t, (__bf16)o);
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

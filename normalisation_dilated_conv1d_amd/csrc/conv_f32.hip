@@ -221,21 +221,34 @@ conv_f32_kernel(ConvF32Args a) {
   XT* __restrict__ outn = reinterpret_cast<XT*>(a.out) + (size_t)n * a.C_out * a.L_out;
   const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
   if (EPI == EPI_RESIDUAL) {
+    // Residual and bias loads use clamped (always in-bounds) addresses and are issued
+    // a 16-channel block at a time before any use, so each block pays the memory
+    // latency once; only the stores are predicated.
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb) {
+      float res[4][NB], bco[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int coc = min(co_base + 16 * mb + r, a.C_out - 1);
+        bco[r] = a.bias ? a.bias[coc] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int tc = min(t0 + 16 * nb + l16, a.L_out - 1);
+          // residual: C_in == C_out and L_in == L_out for the block
+          res[r][nb] = to_f32(xn[coc * a.L_in + tc]);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int co = co_base + 16 * mb + r;
-        if (co < a.C_out) {
-          const float bco = a.bias ? a.bias[co] : 0.f;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int t = t0 + 16 * nb + l16;
-            if (t < a.L_out)
-              from_f32(acc[mb][nb][r] + bco + to_f32(xn[co * a.L_in + t]), &outn[co * a.L_out + t]);
-          }
+        for (int nb = 0; nb < NB; ++nb) {
+          const int t = t0 + 16 * nb + l16;
+          if (co < a.C_out && t < a.L_out)
+            from_f32(acc[mb][nb][r] + bco[r] + res[r][nb], &outn[co * a.L_out + t]);
         }
       }
+    }
   } else {
     const int cnt = min(TT, a.L_out - t0);
     const float inv_cnt = 1.f / (float)cnt;
