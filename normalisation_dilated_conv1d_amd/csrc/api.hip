@@ -152,11 +152,10 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   // bf16 storage runs the bf16-MFMA kernel: 64-channel K-chunks, 128-step time tiles
   const int Cin_pad = round_up(Ci, bf16 ? CIN_PAD_BF16 : KC);
   const int Cout_pad = round_up(Ci, CO_TILE_F32);
-  const int n_ct = Cout_pad / CO_TILE_F32;
-  const int tile_t = bf16 ? TILE_T_BF16
-                          : conv_f32_tile_t(EPI_RESIDUAL, Li,
-                                            (int)std::min<int64_t>(N * n_ct, kMaxIndex));
-  const int n_tt = (Li + tile_t - 1) / tile_t;
+  const ConvTile tile = bf16 ? ConvTile{TILE_T_BF16, 4}
+                             : conv_f32_tile(Li, (int)std::min<int64_t>(N, kMaxIndex), Ci);
+  const int n_ct = (Ci + tile.co_tile() - 1) / tile.co_tile();
+  const int n_tt = (Li + tile.tt - 1) / tile.tt;
   if (N * n_tt * n_ct > kMaxIndex)
     return fail(DCONV1D_EINVAL, "grid of %lld workgroups is too large",
                 (long long)(N * n_tt * n_ct));
@@ -205,7 +204,7 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   a.n_tt = n_tt;
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
-  e = bf16 ? launch_conv_bf16(a, stream) : launch_conv_f32(a, tile_t, EPI_RESIDUAL, stream);
+  e = bf16 ? launch_conv_bf16(a, stream) : launch_conv_f32(a, tile, EPI_RESIDUAL, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
   return DCONV1D_OK;
@@ -266,10 +265,10 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
 
   const int Cin_pad = round_up((int)C_in, KC);
   const int Cout_pad = round_up((int)C_out, CO_TILE_F32);
-  const int n_ct = Cout_pad / CO_TILE_F32;
   const int Lo = (int)T_out;
-  const int tile_t = conv_f32_tile_t(EPI_GN_STATS, Lo, (int)std::min<int64_t>(N * n_ct, kMaxIndex));
-  const int n_tt = (Lo + tile_t - 1) / tile_t;
+  const ConvTile tile = conv_f32_tile(Lo, (int)std::min<int64_t>(N, kMaxIndex), (int)C_out);
+  const int n_ct = ((int)C_out + tile.co_tile() - 1) / tile.co_tile();
+  const int n_tt = (Lo + tile.tt - 1) / tile.tt;
   if (N * n_tt * n_ct > kMaxIndex) return fail(DCONV1D_EINVAL, "grid too large");
   if (N == 0) return DCONV1D_OK;
 
@@ -307,11 +306,11 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
   a.n_tt = n_tt;
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
-  e = launch_conv_f32(a, tile_t, EPI_GN_STATS, stream);
+  e = launch_conv_f32(a, tile, EPI_GN_STATS, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
   e = launch_gn_normalize(out, part, gamma, beta, eps, (int)N, (int)C_out, Lo, (int)num_groups,
-                          n_tt, tile_t, stream);
+                          n_tt, tile.tt, stream);
   if (e != hipSuccess) return hip_fail(e, "groupnorm kernel launch");
   return DCONV1D_OK;
 }

@@ -68,9 +68,10 @@ __device__ __forceinline__ float quarterwave_sum(float v) {
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ void from_f32(float v, float* dst) { *dst = v; }
 
-template <int TT, bool BN, int EPI, typename XT>
+template <int TT, int MB, bool BN, int EPI, typename XT>
 __global__ void __launch_bounds__(NTHREADS, 2)
 conv_f32_kernel(ConvF32Args a) {
+  constexpr int CO_TILE = 4 * 16 * MB;           // output channels per workgroup
   constexpr int NB = TT / 16;                    // 16-column MFMA blocks per wave
   constexpr int NQ = NB / 4;                     // 16-byte LDS reads per MFMA step
   constexpr int CPT = TT / 64;                   // staged columns per thread
@@ -100,11 +101,11 @@ conv_f32_kernel(ConvF32Args a) {
 
   const XT* __restrict__ xn = reinterpret_cast<const XT*>(a.x) + (size_t)n * a.C_in * a.L_in;
   const f32x4* __restrict__ Wp4 = reinterpret_cast<const f32x4*>(a.Wp);
-  const int cb0 = (ct * CO_TILE_F32) / 16 + 4 * w;   // first 16-channel block of the wave
+  const int cb0 = (ct * CO_TILE) / 16 + MB * w;   // first 16-channel block of the wave
 
-  f32x4 acc[4][NB];
+  f32x4 acc[MB][NB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -155,10 +156,10 @@ conv_f32_kernel(ConvF32Args a) {
   // A operands of 16-row group G = 2*chunk + g: 4 float4 (one per 16-channel block),
   // each holding the lane's 4 MFMA steps.
   const int n_groups = 2 * a.Q;
-  auto load_w = [&](int G, f32x4 (&dst)[4]) {
+  auto load_w = [&](int G, f32x4 (&dst)[MB]) {
     G = min(G, n_groups - 1);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) dst[mb] = Wp4[(G * a.NCB + cb0 + mb) * 64 + l];
+    for (int mb = 0; mb < MB; ++mb) dst[mb] = Wp4[(G * a.NCB + cb0 + mb) * 64 + l];
   };
   // B operands of MFMA step s (row 16*(s/4) + 4*lq + s%4).
   auto load_b = [&](const float* zb, int s, f32x4 (&dst)[NQ]) {
@@ -167,7 +168,7 @@ conv_f32_kernel(ConvF32Args a) {
     for (int m = 0; m < NQ; ++m) dst[m] = *reinterpret_cast<const f32x4*>(p + 64 * m);
   };
 
-  f32x4 wr[2][4];
+  f32x4 wr[2][MB];
   f32x4 bv[2][NQ];
 
   auto compute = [&](const float* zb, int q, auto&& mid) {
@@ -181,7 +182,7 @@ conv_f32_kernel(ConvF32Args a) {
         if (s + 1 < 8) load_b(zb, s + 1, bv[(s + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           const float av = wr[g][mb][u];
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
@@ -219,13 +220,13 @@ conv_f32_kernel(ConvF32Args a) {
   // Epilogue. Accumulator register r of block (mb, nb) holds output channel
   // 16*mb + 4*lq + r (within the wave's 64) and time 16*nb + l16.
   XT* __restrict__ outn = reinterpret_cast<XT*>(a.out) + (size_t)n * a.C_out * a.L_out;
-  const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
+  const int co_base = ct * CO_TILE + 16 * MB * w + 4 * lq;
   if (EPI == EPI_RESIDUAL) {
     // Residual and bias loads use clamped (always in-bounds) addresses and are issued
     // a 16-channel block at a time before any use, so each block pays the memory
     // latency once; only the stores are predicated.
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       float res[4][NB], bco[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -253,7 +254,7 @@ conv_f32_kernel(ConvF32Args a) {
     const int cnt = min(TT, a.L_out - t0);
     const float inv_cnt = 1.f / (float)cnt;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int co = co_base + 16 * mb + r;
@@ -291,33 +292,45 @@ conv_f32_kernel(ConvF32Args a) {
   }
 }
 
-// Time-tile width: 128 normally; 64 when 128 would leave the GPU's 256 CUs short of
-// workgroups (small batch x length, as in the GroupNorm workload).
-int conv_f32_tile_t(int epilogue, int L_out, int tiles_other) {
-  (void)epilogue;
-  const long long wg128 = (long long)tiles_other * ((L_out + 127) / 128);
-  return wg128 >= 512 ? 128 : 64;
+// Tile shape. Largest first: 128 time steps x 256 channels (4 accumulator blocks of 16
+// channels per wave) when that gives at least two workgroups per CU (512); otherwise 64
+// time steps; and when even that leaves one wave per SIMD, 64 x 128 channels (2 blocks
+// per wave), which doubles the waves at the cost of reading each x tile twice.
+ConvTile conv_f32_tile(int L_out, int N, int C_out) {
+  auto wgs = [&](int tt, int cot) {
+    return (long long)N * ((L_out + tt - 1) / tt) * ((C_out + cot - 1) / cot);
+  };
+  if (wgs(128, 256) >= 512) return {128, 4};
+  if (wgs(64, 256) >= 512) return {64, 4};
+  return {64, 2};
 }
 
-template <int TT, bool BN, int EPI, typename XT>
+template <int TT, int MB, bool BN, int EPI, typename XT>
 static hipError_t launch_one(const ConvF32Args& a, int nwg, hipStream_t stream) {
-  hipLaunchKernelGGL((conv_f32_kernel<TT, BN, EPI, XT>), dim3(nwg), dim3(NTHREADS), 0, stream, a);
+  hipLaunchKernelGGL((conv_f32_kernel<TT, MB, BN, EPI, XT>), dim3(nwg), dim3(NTHREADS), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
-hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, hipStream_t stream) {
+template <bool BN, int EPI>
+static hipError_t launch_shape(const ConvF32Args& a, ConvTile tile, int nwg, hipStream_t stream) {
+  if (tile.tt == 128 && tile.mb == 4) return launch_one<128, 4, BN, EPI, float>(a, nwg, stream);
+  if (tile.tt == 64 && tile.mb == 4) return launch_one<64, 4, BN, EPI, float>(a, nwg, stream);
+  if (tile.tt == 64 && tile.mb == 2) return launch_one<64, 2, BN, EPI, float>(a, nwg, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv_f32(const ConvF32Args& a, ConvTile tile, int epilogue, hipStream_t stream) {
   const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const bool bn = a.scale != nullptr;
   if (epilogue == EPI_RESIDUAL) {
     if (!bn) return hipErrorInvalidValue;
-    return tile_t == 128 ? launch_one<128, true, EPI_RESIDUAL, float>(a, (int)nwg, stream)
-                         : launch_one<64, true, EPI_RESIDUAL, float>(a, (int)nwg, stream);
+    return launch_shape<true, EPI_RESIDUAL>(a, tile, (int)nwg, stream);
   }
   if (bn) return hipErrorInvalidValue;
-  return tile_t == 128 ? launch_one<128, false, EPI_GN_STATS, float>(a, (int)nwg, stream)
-                       : launch_one<64, false, EPI_GN_STATS, float>(a, (int)nwg, stream);
+  return launch_shape<false, EPI_GN_STATS>(a, tile, (int)nwg, stream);
 }
 
 }  // namespace dconv1d

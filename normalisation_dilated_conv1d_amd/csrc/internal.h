@@ -8,7 +8,8 @@ namespace dconv1d {
 
 // K-chunk: 32 input channels of one tap. One chunk is one LDS stage.
 constexpr int KC = 32;
-// Output channels per workgroup in the float32 kernel: 4 waves x 64 channels.
+// Output channels per workgroup of the largest float32 tile (4 waves x 64 channels),
+// and the padding unit of the repacked output channels.
 constexpr int CO_TILE_F32 = 256;
 constexpr int NTHREADS = 256;
 
@@ -40,8 +41,14 @@ hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, in
                            float* shift, hipStream_t stream);
 
 // conv_f32.hip
-int conv_f32_tile_t(int epilogue, int L_out, int tiles_other);
-hipError_t launch_conv_f32(const ConvF32Args& a, int tile_t, int epilogue, hipStream_t stream);
+// Tile shape of the float32 kernel: tt time steps, 16*mb output channels per wave,
+// 4 waves, so 64*mb output channels per workgroup.
+struct ConvTile {
+  int tt, mb;
+  int co_tile() const { return 64 * mb; }
+};
+ConvTile conv_f32_tile(int L_out, int N, int C_out);
+hipError_t launch_conv_f32(const ConvF32Args& a, ConvTile tile, int epilogue, hipStream_t stream);
 
 // conv_bf16.hip: 64-channel K-chunks, input channels padded to a multiple of 128 (an
 // even chunk count), 128 time steps per tile

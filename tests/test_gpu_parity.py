@@ -95,6 +95,7 @@ BLOCK_CASES = [
     (5, 256, 130, 7),
     (8, 64, 8200, 128),      # 128-wide time tiles with a ragged tail
     (2, 33, 257, 31),
+    (8, 64, 5000, 77),       # 64-step x 256-channel tiles
 ]
 
 
@@ -215,6 +216,8 @@ GN_CASES = [
     (2, 64, 300, 150, 3, 1, 1, False, True),     # two output-channel tiles
     (3, 8, 16, 5, 4, 2, 3, False, True),         # T_out = 3
     (4, 128, 256, 1023, 32, 1, 1, False, True),  # ragged time tail
+    (8, 32, 64, 5000, 8, 1, 1, True, True),      # 64-step x 256-channel tiles
+    (2, 64, 300, 150, 3, 1, 1, False, True),     # 128-channel tiles, 3 channel tiles
 ]
 
 
