@@ -20,8 +20,9 @@
 //   A operand  = weights rounded to bfloat16 by the repack kernel and stored in lane
 //                order: one 16-byte load per (K-step, 16-channel block) per lane, loaded
 //                two K-steps ahead through a 4-slot register ring.
-//   x loads    = when every tap offset and L are even, each lane loads two adjacent time
-//                steps with one aligned 4-byte load; otherwise two 2-byte loads.
+//   x loads    = buffer loads (row offset in an SGPR). When every tap offset and L are
+//                even, each lane loads two adjacent time steps with one aligned 4-byte
+//                load; otherwise two 2-byte loads.
 //
 // K-slot mapping: in K-step s of a chunk, quarter-wave q = lane/16 element e (0..7) is
 // chunk row 32s + 8q + e, for A and B alike, so the sum over K is the plain sum over
@@ -58,6 +59,8 @@ struct Parity {
 };
 
 constexpr int KCB = 64;   // channel rows per chunk (two MFMA K-steps)
+// buffer resource word 3 for raw (untyped, unswizzled) buffers on gfx9-family parts
+constexpr int kBufferFlags = 0x00020000;
 constexpr int TTB = TILE_T_BF16;  // time steps per workgroup
 
 template <bool PAIR>
@@ -102,26 +105,31 @@ conv_bf16_kernel(ConvF32Args a) {
   uint32_t xr[RPW * (PAIR ? 1 : 2)];
   float sc[RPW], sh[RPW];
 
+  // x is read with buffer loads: the wave-uniform row offset goes in an SGPR and the
+  // per-lane time offset is one register per chunk, so a load costs no vector address
+  // arithmetic (the weights stay plain global loads: that measured faster).
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xn), (short)0, a.C_in * a.L_in * 2, kBufferFlags);
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
     const int off = k * a.dil - a.pad;
     if (PAIR) {
       const int ts = t0 + 2 * l + off;
-      const int tsc = min(max(ts, 0), a.L_in - 2);
+      const int vo = 2 * min(max(ts, 0), a.L_in - 2);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
-        xr[i] = *reinterpret_cast<const uint32_t*>(xn + (size_t)ci * a.L_in + tsc);
+        xr[i] = __builtin_amdgcn_raw_buffer_load_b32(xres, vo, ci * a.L_in * 2, 0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int ts = t0 + l + 64 * j + off;
-        const int tsc = min(max(ts, 0), a.L_in - 1);
+        const int vo = 2 * min(max(ts, 0), a.L_in - 1);
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
           const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
-          xr[j * RPW + i] = xn[(size_t)ci * a.L_in + tsc];
+          xr[j * RPW + i] = __builtin_amdgcn_raw_buffer_load_b16(xres, vo, ci * a.L_in * 2, 0);
         }
       }
     }
