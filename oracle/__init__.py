@@ -4,6 +4,7 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE: only ``tests/``, ``__graft_entry__.smoke(
 and ``bench.py``'s ``cpu_baseline`` leg may import this package. The HIP library and
 its Python binding never import or call it.
 """
-from .reference import (bn_eval_relu, conv1d_k3_padded, conv_groupnorm,  # noqa: F401
-                        conv_output_length, group_norm, prenorm_block,
-                        prenorm_block_points, zero_pad_time)
+from .reference import (batch_stats, bn_eval_relu, conv1d_k3_padded,  # noqa: F401
+                        conv_groupnorm, conv_output_length, group_norm, prenorm_block,
+                        prenorm_block_points, prenorm_block_train, running_stats_update,
+                        zero_pad_time)

@@ -150,6 +150,48 @@ def prenorm_block_points(x, running_mean, running_var, gamma, beta, eps, W, b, d
     return out
 
 
+def batch_stats(x):
+    """Per-channel batch mean and biased variance over the batch and time axes, taken
+    two-pass in float64 (POPCORNBENCH "Kimi-K2.6__l2_p97", BatchNorm in training mode:
+    normalise with the batch mean and the biased variance)."""
+    x = _f64(x)
+    mean = x.mean(axis=(0, 2))
+    var = ((x - mean[None, :, None]) ** 2).mean(axis=(0, 2))
+    return mean, var
+
+
+def running_stats_update(running_mean, running_var, batch_mean, batch_var, count: int,
+                         momentum: float):
+    """Training-mode update of the running statistics: an exponential average with weight
+    `momentum` on the new batch, where the running variance takes the unbiased batch
+    variance var * n / (n - 1) (Kimi-K2.6__l2_p97, first turn: running_var is updated
+    with the n/(n-1)-corrected variance, momentum 0.1)."""
+    m = float(momentum)
+    rm = (1.0 - m) * _f64(running_mean) + m * _f64(batch_mean)
+    rv = (1.0 - m) * _f64(running_var) + m * _f64(batch_var) * count / (count - 1)
+    return rm, rv
+
+
+def prenorm_block_train(x, running_mean, running_var, gamma, beta, eps, momentum, W, b,
+                        d: int):
+    """The pre-norm block with BatchNorm1d in training mode.
+
+    BN uses the batch statistics of x (mean and biased variance per channel over N and L)
+    instead of the running ones; the rest of the block is prenorm_block's. Also returns
+    the updated running statistics and the batch statistics:
+    (out, new_running_mean, new_running_var, batch_mean, batch_var).
+    Kimi-K2.6__l2_p12, correctness-debugging turn: the batch-statistics hypothesis for
+    the block (mean over batch and time, unbiased=False); Kimi-K2.6__l2_p97: training-mode
+    semantics and the running-statistics update.
+    """
+    x64 = _f64(x)
+    N, C, L = x64.shape
+    mean, var = batch_stats(x64)
+    out = prenorm_block(x64, mean, var, gamma, beta, eps, W, b, d)
+    rm, rv = running_stats_update(running_mean, running_var, mean, var, N * L, momentum)
+    return out, rm, rv, mean, var
+
+
 def group_norm(y, num_groups: int, gamma, beta, eps):
     """GroupNorm over (N, C, T): groups are contiguous channel blocks of C/num_groups.
 

@@ -218,6 +218,94 @@ BLOCK_PINS = [block_hand_golden, block_brute_tiny, block_torch_f64, block_paddin
               block_one_hot, block_relu_identity, block_linear_in_W, block_output_length]
 
 
+# --------------------------------------------------------------------------- train-mode BN pins
+
+def _call_train(fn, p, d, momentum):
+    out, rm, rv, m, v = fn(p["x"], p["running_mean"], p["running_var"], p["gamma"], p["beta"],
+                           p["eps"], momentum, p["W"], p["b"], d)
+    return _np(out), _np(rm), _np(rv), _np(m), _np(v)
+
+
+def train_hand_golden(fn):
+    g = json.load(open(os.path.join(GOLDEN, "prenorm_block_train_hand.json")))
+    i = g["inputs"]
+    p = {k: (_np(v) if isinstance(v, list) else v) for k, v in i.items()}
+    out, rm, rv, m, v = _call_train(fn, p, i["d"], i["momentum"])
+    err = max(_maxrel(out, g["expected"]), _maxrel(rm, g["expected_running_mean"]),
+              _maxrel(rv, g["expected_running_var"]), _maxrel(m, g["expected_batch_mean"]),
+              _maxrel(v, g["expected_batch_var"]))
+    return err <= 1e-14, f"train hand golden max rel err {err:.3g}"
+
+
+def train_torch_f64(fn):
+    """torch float64 F.batch_norm(training=True) (which updates the running statistics in
+    place), relu, conv1d, residual."""
+    worst = 0.0
+    for (N, C, L, d, mom, seed) in [(2, 16, 512, 128, 0.1, 1), (3, 24, 300, 7, 0.3, 2),
+                                    (1, 8, 50, 60, 0.1, 3), (4, 12, 33, 1, 1.0, 4)]:
+        p = _rand_block(N, C, L, seed, beta_shift=0.2)
+        p["x"] = p["x"] * 1.7 + np.linspace(-1, 2, C)[None, :, None]
+        t = lambda a: torch.from_numpy(np.array(a, dtype=np.float64))
+        rm, rv = t(p["running_mean"]), t(p["running_var"])
+        z = F.relu(F.batch_norm(t(p["x"]), rm, rv, t(p["gamma"]), t(p["beta"]), training=True,
+                                momentum=mom, eps=p["eps"]))
+        exp = t(p["x"]) + F.conv1d(z, t(p["W"]), t(p["b"]), padding=d, dilation=d)
+        out, frm, frv, _, _ = _call_train(fn, p, d, mom)
+        worst = max(worst, _maxrel(out, exp.numpy()), _maxrel(frm, rm.numpy()),
+                    _maxrel(frv, rv.numpy()))
+    return worst <= 1e-10, f"torch float64 training batch_norm max rel err {worst:.3g}"
+
+
+def train_brute_tiny(fn):
+    """Batch statistics by scalar loops, then the brute-force eval block with them."""
+    worst = 0.0
+    for (N, C, L, d, seed) in [(2, 3, 9, 2, 5), (1, 2, 7, 7, 6)]:
+        p = _rand_block(N, C, L, seed, beta_shift=0.3)
+        x = p["x"].tolist()
+        mean, var = [], []
+        for c in range(C):
+            vals = [x[n][c][t] for n in range(N) for t in range(L)]
+            m = sum(vals) / len(vals)
+            mean.append(m)
+            var.append(sum((v - m) ** 2 for v in vals) / len(vals))
+        ref = brute.prenorm_block_brute(p["x"], np.array(mean), np.array(var), p["gamma"],
+                                        p["beta"], p["eps"], p["W"], p["b"], d)
+        out, _, _, m, v = _call_train(fn, p, d, 0.1)
+        worst = max(worst, _maxrel(out, ref), _maxrel(m, mean), _maxrel(v, var))
+    return worst <= 1e-12, f"train brute force max rel err {worst:.3g}"
+
+
+def train_shift_invariance(fn):
+    """Training-mode BN removes a per-channel constant: out(x + c) - (x + c) == out(x) - x."""
+    p = _rand_block(2, 6, 40, 7)
+    shift = np.linspace(-3, 5, 6)[None, :, None]
+    q = dict(p, x=p["x"] + shift)
+    o1 = _call_train(fn, p, 3, 0.1)[0] - p["x"]
+    o2 = _call_train(fn, q, 3, 0.1)[0] - q["x"]
+    err = float(np.max(np.abs(o1 - o2)))
+    return err <= 1e-11, f"train shift invariance max abs err {err:.3g}"
+
+
+def train_momentum_limits(fn):
+    """momentum 0 keeps the running statistics; momentum 1 replaces them with the batch
+    mean and the unbiased batch variance."""
+    p = _rand_block(2, 5, 30, 8)
+    _, rm0, rv0, _, _ = _call_train(fn, p, 2, 0.0)
+    _, rm1, rv1, m, v = _call_train(fn, p, 2, 1.0)
+    n = 2 * 30
+    xs = p["x"].transpose(1, 0, 2).reshape(5, -1)
+    err = max(float(np.max(np.abs(rm0 - p["running_mean"]))),
+              float(np.max(np.abs(rv0 - p["running_var"]))),
+              float(np.max(np.abs(rm1 - xs.mean(axis=1)))),
+              float(np.max(np.abs(rv1 - xs.var(axis=1, ddof=1)))),
+              float(np.max(np.abs(v * n / (n - 1) - xs.var(axis=1, ddof=1)))))
+    return err <= 1e-12, f"momentum limits max abs err {err:.3g}"
+
+
+TRAIN_PINS = [train_hand_golden, train_torch_f64, train_brute_tiny, train_shift_invariance,
+              train_momentum_limits]
+
+
 # --------------------------------------------------------------------------- GroupNorm pins
 
 def _rand_gn(N, C_in, C_out, T, seed, bias=False):

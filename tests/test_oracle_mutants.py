@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from oracle import reference as R
-from pins import BLOCK_PINS, GN_PINS
+from pins import BLOCK_PINS, GN_PINS, TRAIN_PINS
 
 
 def _m_tap_reversed(x, rm, rv, g, b_, eps, W, b, d):
@@ -96,6 +96,40 @@ def _g_stats_per_channel(x, W, bias, gamma, beta, eps, G, padding=1, dilation=1)
 GN_MUTANTS = [_g_unbiased, _g_interleaved_groups, _g_no_beta, _g_no_padding, _g_stats_per_channel]
 
 
+def _t_unbiased_norm(x, rm, rv, g, b_, eps, mom, W, b, d):
+    x64 = R._f64(x)
+    N, C, L = x64.shape
+    mean = x64.mean(axis=(0, 2))
+    var = x64.var(axis=(0, 2), ddof=1)                      # wrong: unbiased for normalising
+    out = oracle.prenorm_block(x64, mean, var, g, b_, eps, W, b, d)
+    nrm, nrv = R.running_stats_update(rm, rv, mean, x64.var(axis=(0, 2)), N * L, mom)
+    return out, nrm, nrv, mean, x64.var(axis=(0, 2))
+
+
+def _t_biased_running(x, rm, rv, g, b_, eps, mom, W, b, d):
+    out, nrm, _, mean, var = oracle.prenorm_block_train(x, rm, rv, g, b_, eps, mom, W, b, d)
+    nrv = (1 - mom) * R._f64(rv) + mom * var                # wrong: no n/(n-1)
+    return out, nrm, nrv, mean, var
+
+
+def _t_stats_over_batch_only(x, rm, rv, g, b_, eps, mom, W, b, d):
+    x64 = R._f64(x)
+    N, C, L = x64.shape
+    mean = x64.mean(axis=(0, 2))
+    var = x64[:, :, :1].var(axis=(0, 2))                    # wrong: statistics of t=0 only
+    out = oracle.prenorm_block(x64, mean, var, g, b_, eps, W, b, d)
+    nrm, nrv = R.running_stats_update(rm, rv, mean, var, N * L, mom)
+    return out, nrm, nrv, mean, var
+
+
+def _t_momentum_swapped(x, rm, rv, g, b_, eps, mom, W, b, d):
+    return oracle.prenorm_block_train(x, rm, rv, g, b_, eps, 1.0 - mom, W, b, d)
+
+
+TRAIN_MUTANTS = [_t_unbiased_norm, _t_biased_running, _t_stats_over_batch_only,
+                 _t_momentum_swapped]
+
+
 def _caught(pins, fn):
     failed = []
     for pin in pins:
@@ -111,6 +145,11 @@ def _caught(pins, fn):
 @pytest.mark.parametrize("mutant", BLOCK_MUTANTS, ids=lambda f: f.__name__)
 def test_block_mutant_is_caught(mutant):
     assert _caught(BLOCK_PINS, mutant), f"no pin rejects {mutant.__name__}"
+
+
+@pytest.mark.parametrize("mutant", TRAIN_MUTANTS, ids=lambda f: f.__name__)
+def test_train_mutant_is_caught(mutant):
+    assert _caught(TRAIN_PINS, mutant), f"no pin rejects {mutant.__name__}"
 
 
 @pytest.mark.parametrize("mutant", GN_MUTANTS, ids=lambda f: f.__name__)
