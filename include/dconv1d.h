@@ -10,6 +10,8 @@
  *      first turn: the block definition, the per-channel eval-mode BN formula with the
  *      running statistics, the conv's zero padding (taps t-d, t, t+d; out-of-range taps
  *      contribute nothing) and the output-length check that gives L_out = L.
+ *      BN runs in eval mode (running statistics) or, in the *_train entry points, in
+ *      training mode (batch statistics and a running-statistics update).
  *
  *   2. Conv1d(k=3, stride 1) followed by GroupNorm.
  *      Source: POPCORNBENCH page "FW-GLM-5-1__l2_p35" (Conv1d + GroupNorm problem), its
@@ -101,6 +103,51 @@ int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
                              const float* running_var, const float* gamma, const float* beta,
                              float eps, const float* W, const float* b, uint16_t* out,
                              int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream);
+
+/*
+ * prenorm_dconv1d_fwd_train - the pre-norm block with BatchNorm1d in training mode.
+ *
+ * Source: POPCORNBENCH page "Kimi-K2.6__l2_p97", first turn (training-mode BatchNorm:
+ * normalise with the batch mean and the biased batch variance; the running mean and
+ * variance move towards the batch mean and the n/(n-1)-corrected batch variance with
+ * weight momentum), and "Kimi-K2.6__l2_p12", correctness-debugging turn (the block
+ * with batch statistics taken per channel over the batch and time axes).
+ *
+ *   x, gamma, beta, eps, W, b, out, N, C, L, d, stream   as in prenorm_dconv1d_fwd
+ *   running_mean device, float32 [C] or NULL   in/out: when given (with running_var),
+ *   running_var  device, float32 [C] or NULL   updated in place with n = N*L:
+ *                  running_mean = (1-momentum)*running_mean + momentum*mean
+ *                  running_var  = (1-momentum)*running_var  + momentum*var*n/(n-1)
+ *                Both NULL: no running update. Only one NULL: DCONV1D_EINVAL.
+ *   momentum     weight of the batch statistics in the running update (finite)
+ *   save_mean    device, float32 [C] or NULL   out: the batch mean
+ *   save_invstd  device, float32 [C] or NULL   out: 1/sqrt(var + eps), biased var
+ *
+ * The batch statistics are mean and biased variance per channel over all N*L values;
+ * N*L must be at least 2 (DCONV1D_EINVAL otherwise; N == 0 is a no-op that leaves
+ * the running statistics unchanged). They are computed by a separate pass over x in
+ * double precision with a fixed reduction order, so results are bitwise reproducible,
+ * and folded into the same scale/shift as the eval-mode call; the conv is then the
+ * eval-mode kernel. The running statistics and the saved vectors must not overlap x,
+ * out or each other (DCONV1D_EALIAS).
+ */
+int prenorm_dconv1d_fwd_train(const float* x, float* running_mean, float* running_var,
+                              const float* gamma, const float* beta, float eps, float momentum,
+                              const float* W, const float* b, float* out,
+                              float* save_mean, float* save_invstd,
+                              int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream);
+
+/*
+ * prenorm_dconv1d_fwd_train_bf16 - the training-mode block with bfloat16 storage of x and
+ * out (uint16_t bit patterns); statistics are taken on the bfloat16 values of x, and the
+ * rest is as in prenorm_dconv1d_fwd_train and prenorm_dconv1d_fwd_bf16.
+ */
+int prenorm_dconv1d_fwd_train_bf16(const uint16_t* x, float* running_mean, float* running_var,
+                                   const float* gamma, const float* beta, float eps,
+                                   float momentum, const float* W, const float* b, uint16_t* out,
+                                   float* save_mean, float* save_invstd,
+                                   int64_t N, int64_t C, int64_t L, int64_t d,
+                                   hipStream_t stream);
 
 /*
  * conv1d_groupnorm_fwd - GroupNorm(Conv1d_{k=3, stride 1}(x)) in float32.

@@ -48,6 +48,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.prenorm_dconv1d_fwd.restype = ctypes.c_int
     lib.prenorm_dconv1d_fwd_bf16.argtypes = [P, P, P, P, P, F, P, P, P, I64, I64, I64, I64, S]
     lib.prenorm_dconv1d_fwd_bf16.restype = ctypes.c_int
+    train_args = [P, P, P, P, P, F, F, P, P, P, P, P, I64, I64, I64, I64, S]
+    lib.prenorm_dconv1d_fwd_train.argtypes = train_args
+    lib.prenorm_dconv1d_fwd_train.restype = ctypes.c_int
+    lib.prenorm_dconv1d_fwd_train_bf16.argtypes = train_args
+    lib.prenorm_dconv1d_fwd_train_bf16.restype = ctypes.c_int
     lib.conv1d_groupnorm_fwd.argtypes = [P, P, P, P, P, F, I64, P, I64, I64, I64, I64, I64, I64, S]
     lib.conv1d_groupnorm_fwd.restype = ctypes.c_int
     lib.dconv1d_last_error.argtypes = []
@@ -138,6 +143,58 @@ def prenorm_dconv1d_fwd_bf16(x, running_mean, running_var, gamma, beta, eps, W, 
     """The same block with bfloat16 x and out (float32 parameters, float32 accumulation)."""
     return _prenorm("prenorm_dconv1d_fwd_bf16", x, running_mean, running_var, gamma, beta, eps,
                     W, b, d, out, torch.bfloat16)
+
+
+def _prenorm_train(fn_name, x, running_mean, running_var, gamma, beta, eps, momentum, W, b, d,
+                   out, save_mean, save_invstd, xdtype):
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (N, C, L)")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    N, C, L = x.shape
+    dev = x.device
+    _dev_tensor("x", x, xdtype, (N, C, L), dev)
+    for name, t in (("running_mean", running_mean), ("running_var", running_var),
+                    ("save_mean", save_mean), ("save_invstd", save_invstd)):
+        if t is not None:
+            _dev_tensor(name, t, torch.float32, (C,), dev)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        _dev_tensor(name, t, torch.float32, (C,), dev)
+    _dev_tensor("W", W, torch.float32, (C, C, 3), dev)
+    if b is not None:
+        _dev_tensor("b", b, torch.float32, (C,), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _dev_tensor("out", out, xdtype, (N, C, L), dev)
+    with torch.cuda.device(dev):
+        code = getattr(lib, fn_name)(_ptr(x), _ptr(running_mean), _ptr(running_var), _ptr(gamma),
+                                     _ptr(beta), float(eps), float(momentum), _ptr(W), _ptr(b),
+                                     _ptr(out), _ptr(save_mean), _ptr(save_invstd), N, C, L,
+                                     int(d), _stream(dev))
+    _check(code)
+    return out
+
+
+def prenorm_dconv1d_fwd_train(x, running_mean, running_var, gamma, beta, eps, momentum, W, b, d,
+                              out=None, save_mean=None, save_invstd=None):
+    """The float32 block with BatchNorm1d in training mode (batch statistics over N and L).
+
+    running_mean / running_var (C,) are updated in place when given (both or neither);
+    save_mean / save_invstd (C,), when given, receive the batch mean and 1/sqrt(var+eps).
+    Returns ``out``."""
+    return _prenorm_train("prenorm_dconv1d_fwd_train", x, running_mean, running_var, gamma,
+                          beta, eps, momentum, W, b, d, out, save_mean, save_invstd,
+                          torch.float32)
+
+
+def prenorm_dconv1d_fwd_train_bf16(x, running_mean, running_var, gamma, beta, eps, momentum, W,
+                                   b, d, out=None, save_mean=None, save_invstd=None):
+    """The training-mode block with bfloat16 x and out."""
+    return _prenorm_train("prenorm_dconv1d_fwd_train_bf16", x, running_mean, running_var, gamma,
+                          beta, eps, momentum, W, b, d, out, save_mean, save_invstd,
+                          torch.bfloat16)
 
 
 def conv1d_groupnorm_fwd(x, W, bias, gamma, beta, eps, num_groups, padding=1, dilation=1,

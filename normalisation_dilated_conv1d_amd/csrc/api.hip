@@ -126,16 +126,31 @@ int check_sizes_block(int64_t N, int64_t C, int64_t L, int64_t d, float eps) {
   return DCONV1D_OK;
 }
 
+// Training-mode BN arguments (null for the eval-mode entry points).
+struct TrainBn {
+  float momentum;
+  float* running_mean;  // nullable together with running_var: no running update
+  float* running_var;
+  float* save_mean;     // nullable
+  float* save_invstd;   // nullable
+};
+
 template <typename XT>
 int prenorm_common(const XT* x, const float* running_mean, const float* running_var,
                    const float* gamma, const float* beta, float eps, const float* W,
                    const float* b, XT* out, int64_t N, int64_t C, int64_t L, int64_t d,
-                   hipStream_t stream, bool bf16) {
+                   hipStream_t stream, bool bf16, const TrainBn* train) {
   // an empty batch has no data: x and out may then be NULL (torch gives empty tensors
   // a null data pointer)
   if (!x && N != 0) return fail(DCONV1D_EINVAL, "x is NULL");
-  if (!running_mean) return fail(DCONV1D_EINVAL, "running_mean is NULL");
-  if (!running_var) return fail(DCONV1D_EINVAL, "running_var is NULL");
+  if (train) {
+    if ((running_mean == nullptr) != (running_var == nullptr))
+      return fail(DCONV1D_EINVAL, "running_mean and running_var must both be given or both NULL");
+    if (!std::isfinite(train->momentum)) return fail(DCONV1D_EINVAL, "momentum must be finite");
+  } else {
+    if (!running_mean) return fail(DCONV1D_EINVAL, "running_mean is NULL");
+    if (!running_var) return fail(DCONV1D_EINVAL, "running_var is NULL");
+  }
   if (!gamma) return fail(DCONV1D_EINVAL, "gamma is NULL");
   if (!beta) return fail(DCONV1D_EINVAL, "beta is NULL");
   if (!W) return fail(DCONV1D_EINVAL, "W is NULL");
@@ -147,6 +162,24 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
     return fail(DCONV1D_EINVAL, "N*C*L overflows");
   const uint64_t bytes = (uint64_t)N * per_sample * sizeof(XT);
   if (overlaps(x, bytes, out, bytes)) return fail(DCONV1D_EALIAS, "out overlaps x");
+  if (train) {
+    if (N != 0 && N * L < 2)
+      return fail(DCONV1D_EINVAL, "training-mode BN needs more than one value per channel "
+                                  "(N*L = %lld)", (long long)(N * L));
+    // vectors written by the statistics pass must not overlap x, out or each other
+    const void* outs[4] = {train->running_mean, train->running_var, train->save_mean,
+                           train->save_invstd};
+    const char* names[4] = {"running_mean", "running_var", "save_mean", "save_invstd"};
+    const uint64_t vb = 4 * (uint64_t)C;
+    for (int i = 0; i < 4; ++i) {
+      if (!outs[i]) continue;
+      if (overlaps(outs[i], vb, x, bytes) || overlaps(outs[i], vb, out, bytes))
+        return fail(DCONV1D_EALIAS, "%s overlaps x or out", names[i]);
+      for (int j = 0; j < i; ++j)
+        if (outs[j] && overlaps(outs[i], vb, outs[j], vb))
+          return fail(DCONV1D_EALIAS, "%s overlaps %s", names[i], names[j]);
+    }
+  }
 
   const int Ci = (int)C, Li = (int)L;
   // bf16 storage runs the bf16-MFMA kernel: 64-channel K-chunks, 128-step time tiles
@@ -159,6 +192,8 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   if (N * n_tt * n_ct > kMaxIndex)
     return fail(DCONV1D_EINVAL, "grid of %lld workgroups is too large",
                 (long long)(N * n_tt * n_ct));
+  if (train && N * C * ((L + STAT_SEG - 1) / STAT_SEG) > kMaxIndex)
+    return fail(DCONV1D_EINVAL, "statistics grid is too large");
   if (N == 0) return DCONV1D_OK;
 
   // d >= L: both outer taps are always in the padding; d = L gives the same result and
@@ -169,7 +204,9 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   const size_t off_scale = 0;
   const size_t off_shift = align256(off_scale + sizeof(float) * Cin_pad);
   const size_t off_wp = align256(off_shift + sizeof(float) * Cin_pad);
-  const size_t total = align256(off_wp + wp_bytes);
+  const size_t off_part = align256(off_wp + wp_bytes);
+  const size_t part_bytes = train ? bn_train_partials_bytes((int)N, Ci, Li) : 0;
+  const size_t total = align256(off_part + part_bytes);
   char* ws = nullptr;
   st = get_workspace(total, &ws);
   if (st != DCONV1D_OK) return st;
@@ -177,11 +214,20 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   float* shift = reinterpret_cast<float*>(ws + off_shift);
   void* Wp = ws + off_wp;
 
-  hipError_t e =
-      bf16 ? launch_prep_bf16(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var, gamma,
-                              beta, eps, scale, shift, stream)
+  hipError_t e;
+  if (train) {
+    e = launch_bn_train(x, bf16, (int)N, Ci, Li, Cin_pad, ws + off_part, gamma, beta, eps,
+                        train->momentum, train->running_mean, train->running_var,
+                        train->save_mean, train->save_invstd, scale, shift, stream);
+    if (e != hipSuccess) return hip_fail(e, "batch statistics kernel launch");
+  }
+  // eval mode folds the running statistics here; training mode only repacks W
+  float* fold_scale = train ? nullptr : scale;
+  float* fold_shift = train ? nullptr : shift;
+  e = bf16 ? launch_prep_bf16(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var, gamma,
+                              beta, eps, fold_scale, fold_shift, stream)
            : launch_prep_f32(W, Ci, Ci, Cout_pad, Cin_pad, static_cast<float*>(Wp), running_mean,
-                             running_var, gamma, beta, eps, scale, shift, stream);
+                             running_var, gamma, beta, eps, fold_scale, fold_shift, stream);
   if (e != hipSuccess) return hip_fail(e, "prep kernel launch");
 
   ConvF32Args a{};
@@ -220,7 +266,7 @@ int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* 
                         hipStream_t stream) {
   g_err.clear();
   return prenorm_common<float>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N, C,
-                               L, d, stream, false);
+                               L, d, stream, false, nullptr);
 }
 
 int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
@@ -229,7 +275,29 @@ int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
                              int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream) {
   g_err.clear();
   return prenorm_common<uint16_t>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
-                                  C, L, d, stream, true);
+                                  C, L, d, stream, true, nullptr);
+}
+
+int prenorm_dconv1d_fwd_train(const float* x, float* running_mean, float* running_var,
+                              const float* gamma, const float* beta, float eps, float momentum,
+                              const float* W, const float* b, float* out, float* save_mean,
+                              float* save_invstd, int64_t N, int64_t C, int64_t L, int64_t d,
+                              hipStream_t stream) {
+  g_err.clear();
+  const TrainBn t{momentum, running_mean, running_var, save_mean, save_invstd};
+  return prenorm_common<float>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N, C,
+                               L, d, stream, false, &t);
+}
+
+int prenorm_dconv1d_fwd_train_bf16(const uint16_t* x, float* running_mean, float* running_var,
+                                   const float* gamma, const float* beta, float eps,
+                                   float momentum, const float* W, const float* b, uint16_t* out,
+                                   float* save_mean, float* save_invstd, int64_t N, int64_t C,
+                                   int64_t L, int64_t d, hipStream_t stream) {
+  g_err.clear();
+  const TrainBn t{momentum, running_mean, running_var, save_mean, save_invstd};
+  return prenorm_common<uint16_t>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
+                                  C, L, d, stream, true, &t);
 }
 
 int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, const float* gamma,

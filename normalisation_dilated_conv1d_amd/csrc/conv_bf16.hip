@@ -293,7 +293,8 @@ conv_bf16_kernel(ConvF32Args a) {
 }
 
 // Per-call preparation for the bf16 kernel, one launch: the BN fold (as in prep.hip:
-// scale = gamma/sqrt(var+eps), shift = beta - mean*scale, in double, rounded once) and
+// scale = gamma/sqrt(var+eps), shift = beta - mean*scale, in double, rounded once;
+// skipped when scale is null, as in training mode where the statistics pass folds) and
 // the weight repack W[C_out][C_in][3] float32 -> bfloat16 (round to nearest even) in
 // A-operand lane order. Unit (16 bytes) index (S*NCB + cb)*64 + lane, with S = 2*q + s
 // the global K-step (chunk q = 3*c + k: channel block c of 64, tap k) and cb the
@@ -326,7 +327,7 @@ prep_bf16_kernel(const float* __restrict__ W, int C_out, int C_in, int NCB, int 
                h[6] | (h[7] << 16)};
     Wp[idx] = o;
   }
-  if (idx < Cin_pad) {
+  if (scale != nullptr && idx < Cin_pad) {
     float sc = 0.f, sh = 0.f;
     if (idx < C_in) {
       const double sd = (double)gamma[idx] / sqrt((double)var[idx] + (double)eps);

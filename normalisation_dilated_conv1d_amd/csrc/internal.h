@@ -61,6 +61,20 @@ hipError_t launch_prep_bf16(const float* W, int C_out, int C_in, int Cout_pad, i
                             float* shift, hipStream_t stream);
 hipError_t launch_conv_bf16(const ConvF32Args& a, hipStream_t stream);
 
+// bn_train.hip: training-mode BN statistics. Time steps of one (n, c) row per
+// statistics workgroup; the partials hold one (sum, sum of squares) double pair per
+// (channel, n, segment).
+constexpr int STAT_SEG = 4096;
+size_t bn_train_partials_bytes(int N, int C, int L);
+// Writes scale/shift for channels [0, Cin_pad) (zero past C) from the batch statistics
+// of x (float32, or bfloat16 bits when bf16), updates the running statistics when
+// running_mean is non-null and stores the batch mean / inverse std when asked.
+hipError_t launch_bn_train(const void* x, bool bf16, int N, int C, int L, int Cin_pad,
+                           void* partials, const float* gamma, const float* beta, float eps,
+                           float momentum, float* running_mean, float* running_var,
+                           float* save_mean, float* save_invstd, float* scale, float* shift,
+                           hipStream_t stream);
+
 // gn.hip
 hipError_t launch_gn_normalize(float* out, const float* partials, const float* gamma,
                                const float* beta, float eps, int N, int C_out, int L_out,

@@ -10,7 +10,8 @@ import normalisation_dilated_conv1d_amd as dc
 pytestmark = pytest.mark.skipif(not __import__("os").path.exists(dc.LIB_PATH),
                                 reason="libdconv1d.so not built")
 
-EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_bf16", "conv1d_groupnorm_fwd",
+EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_bf16", "prenorm_dconv1d_fwd_train",
+            "prenorm_dconv1d_fwd_train_bf16", "conv1d_groupnorm_fwd",
             "dconv1d_last_error", "dconv1d_release", "dconv1d_timer_enable",
             "dconv1d_timer_read"}
 
@@ -62,6 +63,35 @@ def test_block_null_bias_is_valid_argument():
     lib = dc.load_library()
     # an empty batch with b = NULL passes validation and issues no work
     assert _block(lib, N=0, b=None) == dc.DCONV1D_OK
+
+
+FAKE_RM = 0x40000000
+FAKE_RV = 0x40001000
+
+
+def _train(lib, fn="prenorm_dconv1d_fwd_train", x=FAKE_X, out=FAKE_OUT, rm=FAKE_RM, rv=FAKE_RV,
+           sm=None, si=None, N=2, C=16, L=512, d=128, eps=1e-5, mom=0.1, W=FAKE_P):
+    return getattr(lib, fn)(x, rm, rv, FAKE_P, FAKE_P, eps, mom, W, None, out, sm, si, N, C, L,
+                            d, None)
+
+
+@pytest.mark.parametrize("fn", ["prenorm_dconv1d_fwd_train", "prenorm_dconv1d_fwd_train_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), dc.DCONV1D_EINVAL), (dict(out=None), dc.DCONV1D_EINVAL),
+    (dict(W=None), dc.DCONV1D_EINVAL), (dict(rm=None), dc.DCONV1D_EINVAL),
+    (dict(rv=None), dc.DCONV1D_EINVAL), (dict(mom=float("nan")), dc.DCONV1D_EINVAL),
+    (dict(mom=float("inf")), dc.DCONV1D_EINVAL),
+    (dict(N=1, L=1), dc.DCONV1D_EINVAL),                 # one value per channel
+    (dict(rm=FAKE_OUT + 64), dc.DCONV1D_EALIAS), (dict(sm=FAKE_X), dc.DCONV1D_EALIAS),
+    (dict(si=FAKE_RV + 32), dc.DCONV1D_EALIAS), (dict(out=FAKE_X + 8), dc.DCONV1D_EALIAS),
+    (dict(N=0), dc.DCONV1D_OK), (dict(N=0, x=None, out=None, rm=None, rv=None), dc.DCONV1D_OK),
+    (dict(N=0, rm=None, rv=None, sm=FAKE_P, si=FAKE_P + 4096), dc.DCONV1D_OK),
+])
+def test_train_validation(fn, kw, code):
+    lib = dc.load_library()
+    assert _train(lib, fn=fn, **kw) == code
+    if code != dc.DCONV1D_OK:
+        assert lib.dconv1d_last_error().decode()
 
 
 def _gn(lib, x=FAKE_X, out=FAKE_OUT, N=16, C_in=128, C_out=256, T=1024, G=32, p=1, dil=1,
