@@ -6,5 +6,5 @@ its Python binding never import or call it.
 """
 from .reference import (batch_stats, bn_eval_relu, conv1d_k3_padded,  # noqa: F401
                         conv_groupnorm, conv_output_length, group_norm, prenorm_block,
-                        prenorm_block_points, prenorm_block_train, running_stats_update,
-                        zero_pad_time)
+                        prenorm_block_points, prenorm_block_train, relu_conv_residual,
+                        running_stats_update, zero_pad_time)

@@ -53,6 +53,24 @@ def prenorm_block_brute(x, running_mean, running_var, gamma, beta, eps, W, b, d)
     return out
 
 
+def relu_conv_residual_brute(xn, W, b, residual, d):
+    xn, W, r = _tolist(xn), _tolist(W), _tolist(residual)
+    bb = _tolist(b)
+    N, C, L = len(xn), len(xn[0]), len(xn[0][0])
+    out = [[[0.0] * L for _ in range(C)] for _ in range(N)]
+    for n in range(N):
+        for co in range(C):
+            for t in range(L):
+                acc = 0.0 if bb is None else bb[co]
+                for ci in range(C):
+                    for k in range(3):
+                        t_in = t - d + k * d
+                        if 0 <= t_in < L:
+                            acc += W[co][ci][k] * max(xn[n][ci][t_in], 0.0)
+                out[n][co][t] = r[n][co][t] + acc
+    return out
+
+
 def conv_groupnorm_brute(x, W, bias, gamma, beta, eps, num_groups, padding=1, dilation=1):
     x, W = _tolist(x), _tolist(W)
     bias, gamma, beta = _tolist(bias), _tolist(gamma), _tolist(beta)

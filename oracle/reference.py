@@ -150,6 +150,26 @@ def prenorm_block_points(x, running_mean, running_var, gamma, beta, eps, W, b, d
     return out
 
 
+def relu_conv_residual(xn, W, b, residual, d: int):
+    """out = residual + Conv1d_{k=3, dilation=d, padding=d}(ReLU(xn)).
+
+    The block with its normalisation done by the caller (POPCORNBENCH "Kimi-K2.6__l2_p12",
+    correctness-debugging turn: the fallback that leaves BN to the framework, so that it
+    follows the module's train/eval mode, and fuses ReLU, the conv and the residual add
+    from the block's input, passed separately). The conv input is zero-padded after
+    the ReLU, as in prenorm_block.
+    """
+    xn64 = _f64(xn)
+    N, C, L = xn64.shape
+    z = np.maximum(xn64, 0.0)
+    zpad = zero_pad_time(z, d)
+    L_out = conv_output_length(L, padding=d, dilation=d)
+    y = conv1d_k3_padded(zpad, W, b, d, L_out)
+    res = _f64(residual)
+    assert res.shape == y.shape, (res.shape, y.shape)
+    return res + y
+
+
 def batch_stats(x):
     """Per-channel batch mean and biased variance over the batch and time axes, taken
     two-pass in float64 (POPCORNBENCH "Kimi-K2.6__l2_p97", BatchNorm in training mode:

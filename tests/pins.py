@@ -218,6 +218,78 @@ BLOCK_PINS = [block_hand_golden, block_brute_tiny, block_torch_f64, block_paddin
               block_one_hot, block_relu_identity, block_linear_in_W, block_output_length]
 
 
+# --------------------------------------------------------------------------- external-BN pins
+
+def _rand_ext(N, C, L, seed):
+    rng = np.random.default_rng(seed)
+    return dict(xn=rng.standard_normal((N, C, L)) + 0.2,
+                W=rng.normal(0, 1 / math.sqrt(3 * C), (C, C, 3)),
+                b=rng.normal(0, 0.1, C),
+                residual=rng.standard_normal((N, C, L)))
+
+
+def _call_ext(fn, p, d):
+    return _np(fn(p["xn"], p["W"], p["b"], p["residual"], d))
+
+
+def ext_hand_golden(fn):
+    g = json.load(open(os.path.join(GOLDEN, "relu_conv_residual_hand.json")))
+    i = {k: _np(v) for k, v in g["inputs"].items()}
+    err = max(_maxrel(_call_ext(fn, i, c["d"]), c["expected"]) for c in g["cases"])
+    return err <= 1e-14, f"external-BN hand golden max rel err {err:.3g}"
+
+
+def ext_brute_tiny(fn):
+    worst = 0.0
+    for (N, C, L, ds, seed) in [(1, 2, 6, (1, 2, 5, 6, 9), 1), (2, 3, 11, (1, 3, 10), 2)]:
+        for d in ds:
+            p = _rand_ext(N, C, L, seed * 10 + d)
+            ref = brute.relu_conv_residual_brute(p["xn"], p["W"], p["b"], p["residual"], d)
+            worst = max(worst, _maxrel(_call_ext(fn, p, d), ref))
+    return worst <= 1e-12, f"external-BN brute force max rel err {worst:.3g}"
+
+
+def ext_torch_f64(fn):
+    worst = 0.0
+    for (N, C, L, d, seed) in [(2, 16, 512, 128, 3), (1, 40, 300, 1, 4), (2, 24, 100, 150, 5)]:
+        p = _rand_ext(N, C, L, seed)
+        t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+        exp = t(p["residual"]) + F.conv1d(F.relu(t(p["xn"])), t(p["W"]), t(p["b"]), padding=d,
+                                          dilation=d)
+        worst = max(worst, _maxrel(_call_ext(fn, p, d), exp.numpy()))
+    return worst <= 1e-10, f"external-BN torch float64 max rel err {worst:.3g}"
+
+
+def ext_is_block_with_bn_outside(fn):
+    """With xn = BatchNorm1d_eval(x) (scalar loops) and residual = x, the result is the
+    pre-norm block (brute force)."""
+    N, C, L, d = 2, 3, 10, 3
+    p = _rand_block(N, C, L, 61, beta_shift=0.2)
+    x = p["x"]
+    xn = (p["gamma"][None, :, None] * (x - p["running_mean"][None, :, None])
+          / np.sqrt(p["running_var"][None, :, None] + p["eps"]) + p["beta"][None, :, None])
+    ref = brute.prenorm_block_brute(x, p["running_mean"], p["running_var"], p["gamma"],
+                                    p["beta"], p["eps"], p["W"], p["b"], d)
+    err = _maxrel(_np(fn(xn, p["W"], p["b"], x, d)), ref)
+    return err <= 1e-12, f"external-BN = block with BN outside, max rel err {err:.3g}"
+
+
+def ext_residual_passthrough(fn):
+    """out - residual does not depend on residual, and W = 0 gives residual + b exactly."""
+    p = _rand_ext(2, 5, 30, 62)
+    q = dict(p, residual=p["residual"] * 3.0 - 1.0)
+    a = _call_ext(fn, p, 4) - p["residual"]
+    b = _call_ext(fn, q, 4) - q["residual"]
+    err = float(np.max(np.abs(a - b)))
+    z = dict(p, W=np.zeros_like(p["W"]))
+    err0 = float(np.max(np.abs(_call_ext(fn, z, 4) - (p["residual"] + p["b"][None, :, None]))))
+    return err <= 1e-12 and err0 == 0.0, f"residual passthrough err {err:.3g}, W=0 err {err0:.3g}"
+
+
+EXT_PINS = [ext_hand_golden, ext_brute_tiny, ext_torch_f64, ext_is_block_with_bn_outside,
+            ext_residual_passthrough]
+
+
 # --------------------------------------------------------------------------- train-mode BN pins
 
 def _call_train(fn, p, d, momentum):

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from oracle import reference as R
-from pins import BLOCK_PINS, GN_PINS, TRAIN_PINS
+from pins import BLOCK_PINS, EXT_PINS, GN_PINS, TRAIN_PINS
 
 
 def _m_tap_reversed(x, rm, rv, g, b_, eps, W, b, d):
@@ -130,6 +130,27 @@ TRAIN_MUTANTS = [_t_unbiased_norm, _t_biased_running, _t_stats_over_batch_only,
                  _t_momentum_swapped]
 
 
+def _e_residual_from_input(xn, W, b, residual, d):
+    return oracle.relu_conv_residual(xn, W, b, xn, d)      # wrong: residual = conv input
+
+
+def _e_no_relu(xn, W, b, residual, d):
+    xn64 = R._f64(xn)
+    y = R.conv1d_k3_padded(R.zero_pad_time(xn64, d), W, b, d, xn64.shape[2])   # wrong
+    return R._f64(residual) + y
+
+
+def _e_tap_reversed(xn, W, b, residual, d):
+    return oracle.relu_conv_residual(xn, R._f64(W)[:, :, ::-1], b, residual, d)
+
+
+def _e_bias_dropped(xn, W, b, residual, d):
+    return oracle.relu_conv_residual(xn, W, None, residual, d)
+
+
+EXT_MUTANTS = [_e_residual_from_input, _e_no_relu, _e_tap_reversed, _e_bias_dropped]
+
+
 def _caught(pins, fn):
     failed = []
     for pin in pins:
@@ -145,6 +166,11 @@ def _caught(pins, fn):
 @pytest.mark.parametrize("mutant", BLOCK_MUTANTS, ids=lambda f: f.__name__)
 def test_block_mutant_is_caught(mutant):
     assert _caught(BLOCK_PINS, mutant), f"no pin rejects {mutant.__name__}"
+
+
+@pytest.mark.parametrize("mutant", EXT_MUTANTS, ids=lambda f: f.__name__)
+def test_external_bn_mutant_is_caught(mutant):
+    assert _caught(EXT_PINS, mutant), f"no pin rejects {mutant.__name__}"
 
 
 @pytest.mark.parametrize("mutant", TRAIN_MUTANTS, ids=lambda f: f.__name__)

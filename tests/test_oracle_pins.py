@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from pins import BLOCK_PINS, GN_PINS, TRAIN_PINS, block_brute_config0, _rand_block
+from pins import BLOCK_PINS, EXT_PINS, GN_PINS, TRAIN_PINS, block_brute_config0, _rand_block
 
 
 @pytest.mark.parametrize("pin", BLOCK_PINS, ids=lambda f: f.__name__)
@@ -15,6 +15,12 @@ def test_block_pin(pin):
 
 def test_block_brute_config0():
     ok, msg = block_brute_config0(oracle.prenorm_block)
+    assert ok, msg
+
+
+@pytest.mark.parametrize("pin", EXT_PINS, ids=lambda f: f.__name__)
+def test_external_bn_pin(pin):
+    ok, msg = pin(oracle.relu_conv_residual)
     assert ok, msg
 
 
