@@ -10,8 +10,10 @@
  *      first turn: the block definition, the per-channel eval-mode BN formula with the
  *      running statistics, the conv's zero padding (taps t-d, t, t+d; out-of-range taps
  *      contribute nothing) and the output-length check that gives L_out = L.
- *      BN runs in eval mode (running statistics) or, in the *_train entry points, in
- *      training mode (batch statistics and a running-statistics update).
+ *      BN runs in eval mode (running statistics), in the *_train entry points in
+ *      training mode (batch statistics and a running-statistics update), or, in the
+ *      relu_dconv1d_residual_* entry points, outside the library (the caller passes the
+ *      normalised activation and the residual separately).
  *
  *   2. Conv1d(k=3, stride 1) followed by GroupNorm.
  *      Source: POPCORNBENCH page "FW-GLM-5-1__l2_p35" (Conv1d + GroupNorm problem), its
@@ -146,6 +148,42 @@ int prenorm_dconv1d_fwd_train_bf16(const uint16_t* x, float* running_mean, float
                                    const float* gamma, const float* beta, float eps,
                                    float momentum, const float* W, const float* b, uint16_t* out,
                                    float* save_mean, float* save_invstd,
+                                   int64_t N, int64_t C, int64_t L, int64_t d,
+                                   hipStream_t stream);
+
+/*
+ * relu_dconv1d_residual_fwd - the block with the normalisation done by the caller:
+ *        out = residual + Conv1d_{k=3, dilation=d, padding=d}(ReLU(xn))
+ *
+ * Source: POPCORNBENCH page "Kimi-K2.6__l2_p12", correctness-debugging turn: the
+ * fallback that leaves BatchNorm to the framework (so it follows the module's train or
+ * eval mode and keeps its running statistics) and fuses ReLU, the conv and the residual
+ * add of the block input, which is passed separately from the normalised activation.
+ *
+ *   xn        device, float32 [N][C][L]          normalised activation (the conv input
+ *                                                before ReLU)
+ *   W, b      as in prenorm_dconv1d_fwd
+ *   residual  device, float32 [N][C][L]          added to the conv output (the block's x)
+ *   out       device, float32 [N][C][L]          result; must not overlap xn. It may be
+ *                                                residual itself (in-place residual add),
+ *                                                but not partially overlap it
+ *                                                (DCONV1D_EALIAS)
+ *   N, C, L, d, stream                            as in prenorm_dconv1d_fwd
+ *
+ * The conv input is zero-padded after the ReLU (padded taps contribute exactly 0), and
+ * the arithmetic is that of prenorm_dconv1d_fwd with the BN step removed.
+ */
+int relu_dconv1d_residual_fwd(const float* xn, const float* W, const float* b,
+                              const float* residual, float* out,
+                              int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream);
+
+/*
+ * relu_dconv1d_residual_fwd_bf16 - the same with bfloat16 storage of xn, residual and out
+ * (uint16_t bit patterns); W and b stay float32, the arithmetic is that of
+ * prenorm_dconv1d_fwd_bf16 with the BN step removed.
+ */
+int relu_dconv1d_residual_fwd_bf16(const uint16_t* xn, const float* W, const float* b,
+                                   const uint16_t* residual, uint16_t* out,
                                    int64_t N, int64_t C, int64_t L, int64_t d,
                                    hipStream_t stream);
 

@@ -53,6 +53,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.prenorm_dconv1d_fwd_train.restype = ctypes.c_int
     lib.prenorm_dconv1d_fwd_train_bf16.argtypes = train_args
     lib.prenorm_dconv1d_fwd_train_bf16.restype = ctypes.c_int
+    ext_args = [P, P, P, P, P, I64, I64, I64, I64, S]
+    lib.relu_dconv1d_residual_fwd.argtypes = ext_args
+    lib.relu_dconv1d_residual_fwd.restype = ctypes.c_int
+    lib.relu_dconv1d_residual_fwd_bf16.argtypes = ext_args
+    lib.relu_dconv1d_residual_fwd_bf16.restype = ctypes.c_int
     lib.conv1d_groupnorm_fwd.argtypes = [P, P, P, P, P, F, I64, P, I64, I64, I64, I64, I64, I64, S]
     lib.conv1d_groupnorm_fwd.restype = ctypes.c_int
     lib.dconv1d_last_error.argtypes = []
@@ -194,6 +199,42 @@ def prenorm_dconv1d_fwd_train_bf16(x, running_mean, running_var, gamma, beta, ep
     """The training-mode block with bfloat16 x and out."""
     return _prenorm_train("prenorm_dconv1d_fwd_train_bf16", x, running_mean, running_var, gamma,
                           beta, eps, momentum, W, b, d, out, save_mean, save_invstd,
+                          torch.bfloat16)
+
+
+def _relu_residual(fn_name, xn, W, b, residual, d, out, xdtype):
+    lib = load_library()
+    if xn.dim() != 3:
+        raise ValueError("xn must be (N, C, L)")
+    if not xn.is_cuda:
+        raise ValueError("xn must be a device tensor")
+    N, C, L = xn.shape
+    dev = xn.device
+    _dev_tensor("xn", xn, xdtype, (N, C, L), dev)
+    _dev_tensor("residual", residual, xdtype, (N, C, L), dev)
+    _dev_tensor("W", W, torch.float32, (C, C, 3), dev)
+    if b is not None:
+        _dev_tensor("b", b, torch.float32, (C,), dev)
+    if out is None:
+        out = torch.empty_like(xn)
+    else:
+        _dev_tensor("out", out, xdtype, (N, C, L), dev)
+    with torch.cuda.device(dev):
+        code = getattr(lib, fn_name)(_ptr(xn), _ptr(W), _ptr(b), _ptr(residual), _ptr(out), N, C,
+                                     L, int(d), _stream(dev))
+    _check(code)
+    return out
+
+
+def relu_dconv1d_residual_fwd(xn, W, b, residual, d, out=None):
+    """out = residual + Conv1d_{k=3, dilation=d, padding=d}(ReLU(xn)), float32, with the
+    normalisation done by the caller. ``out`` may be ``residual`` (in-place add)."""
+    return _relu_residual("relu_dconv1d_residual_fwd", xn, W, b, residual, d, out, torch.float32)
+
+
+def relu_dconv1d_residual_fwd_bf16(xn, W, b, residual, d, out=None):
+    """The same with bfloat16 xn, residual and out."""
+    return _relu_residual("relu_dconv1d_residual_fwd_bf16", xn, W, b, residual, d, out,
                           torch.bfloat16)
 
 

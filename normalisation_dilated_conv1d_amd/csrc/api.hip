@@ -135,15 +135,23 @@ struct TrainBn {
   float* save_invstd;   // nullable
 };
 
+// How the block's conv input is normalised.
+enum class Norm { Eval, Train, External };
+
+// The three block variants. x is the conv input and residual the tensor added to the
+// conv output (x itself for Eval and Train; for External x is the caller's normalised
+// activation, and gamma, beta and the running statistics are unused).
 template <typename XT>
-int prenorm_common(const XT* x, const float* running_mean, const float* running_var,
-                   const float* gamma, const float* beta, float eps, const float* W,
-                   const float* b, XT* out, int64_t N, int64_t C, int64_t L, int64_t d,
-                   hipStream_t stream, bool bf16, const TrainBn* train) {
+int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
+                   const float* running_var, const float* gamma, const float* beta, float eps,
+                   const float* W, const float* b, XT* out, int64_t N, int64_t C, int64_t L,
+                   int64_t d, hipStream_t stream, bool bf16, Norm norm, const TrainBn* train) {
   // an empty batch has no data: x and out may then be NULL (torch gives empty tensors
   // a null data pointer)
   if (!x && N != 0) return fail(DCONV1D_EINVAL, "x is NULL");
-  if (train) {
+  if (norm == Norm::External) {
+    if (!residual && N != 0) return fail(DCONV1D_EINVAL, "residual is NULL");
+  } else if (train) {
     if ((running_mean == nullptr) != (running_var == nullptr))
       return fail(DCONV1D_EINVAL, "running_mean and running_var must both be given or both NULL");
     if (!std::isfinite(train->momentum)) return fail(DCONV1D_EINVAL, "momentum must be finite");
@@ -151,8 +159,10 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
     if (!running_mean) return fail(DCONV1D_EINVAL, "running_mean is NULL");
     if (!running_var) return fail(DCONV1D_EINVAL, "running_var is NULL");
   }
-  if (!gamma) return fail(DCONV1D_EINVAL, "gamma is NULL");
-  if (!beta) return fail(DCONV1D_EINVAL, "beta is NULL");
+  if (norm != Norm::External) {
+    if (!gamma) return fail(DCONV1D_EINVAL, "gamma is NULL");
+    if (!beta) return fail(DCONV1D_EINVAL, "beta is NULL");
+  }
   if (!W) return fail(DCONV1D_EINVAL, "W is NULL");
   if (!out && N != 0) return fail(DCONV1D_EINVAL, "out is NULL");
   int st = check_sizes_block(N, C, L, d, eps);
@@ -161,7 +171,12 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   if (N > INT64_MAX / (per_sample * (int64_t)sizeof(XT)))
     return fail(DCONV1D_EINVAL, "N*C*L overflows");
   const uint64_t bytes = (uint64_t)N * per_sample * sizeof(XT);
-  if (overlaps(x, bytes, out, bytes)) return fail(DCONV1D_EALIAS, "out overlaps x");
+  if (overlaps(x, bytes, out, bytes))
+    return fail(DCONV1D_EALIAS, norm == Norm::External ? "out overlaps xn" : "out overlaps x");
+  // out may be the residual itself (each element is read by the thread that writes
+  // it), but not a shifted view of it
+  if (norm == Norm::External && out != residual && overlaps(residual, bytes, out, bytes))
+    return fail(DCONV1D_EALIAS, "out partially overlaps residual");
   if (train) {
     if (N != 0 && N * L < 2)
       return fail(DCONV1D_EINVAL, "training-mode BN needs more than one value per channel "
@@ -221,13 +236,15 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
                         train->save_mean, train->save_invstd, scale, shift, stream);
     if (e != hipSuccess) return hip_fail(e, "batch statistics kernel launch");
   }
-  // eval mode folds the running statistics here; training mode only repacks W
+  // Eval folds the running statistics here, External gets scale 1 / shift 0 (null
+  // gamma), and Train only repacks W (the statistics pass folded already).
   float* fold_scale = train ? nullptr : scale;
   float* fold_shift = train ? nullptr : shift;
-  e = bf16 ? launch_prep_bf16(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var, gamma,
-                              beta, eps, fold_scale, fold_shift, stream)
+  const float* fold_gamma = norm == Norm::External ? nullptr : gamma;
+  e = bf16 ? launch_prep_bf16(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var,
+                              fold_gamma, beta, eps, fold_scale, fold_shift, stream)
            : launch_prep_f32(W, Ci, Ci, Cout_pad, Cin_pad, static_cast<float*>(Wp), running_mean,
-                             running_var, gamma, beta, eps, fold_scale, fold_shift, stream);
+                             running_var, fold_gamma, beta, eps, fold_scale, fold_shift, stream);
   if (e != hipSuccess) return hip_fail(e, "prep kernel launch");
 
   ConvF32Args a{};
@@ -237,6 +254,7 @@ int prenorm_common(const XT* x, const float* running_mean, const float* running_
   a.Wp = static_cast<const float*>(Wp);
   a.bias = b;
   a.out = out;
+  a.residual = norm == Norm::External ? residual : x;
   a.partials = nullptr;
   a.N = (int)N;
   a.C_in = Ci;
@@ -265,8 +283,8 @@ int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* 
                         const float* b, float* out, int64_t N, int64_t C, int64_t L, int64_t d,
                         hipStream_t stream) {
   g_err.clear();
-  return prenorm_common<float>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N, C,
-                               L, d, stream, false, nullptr);
+  return prenorm_common<float>(x, x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
+                               C, L, d, stream, false, Norm::Eval, nullptr);
 }
 
 int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
@@ -274,8 +292,8 @@ int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,
                              float eps, const float* W, const float* b, uint16_t* out,
                              int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream) {
   g_err.clear();
-  return prenorm_common<uint16_t>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
-                                  C, L, d, stream, true, nullptr);
+  return prenorm_common<uint16_t>(x, x, running_mean, running_var, gamma, beta, eps, W, b, out,
+                                  N, C, L, d, stream, true, Norm::Eval, nullptr);
 }
 
 int prenorm_dconv1d_fwd_train(const float* x, float* running_mean, float* running_var,
@@ -285,8 +303,8 @@ int prenorm_dconv1d_fwd_train(const float* x, float* running_mean, float* runnin
                               hipStream_t stream) {
   g_err.clear();
   const TrainBn t{momentum, running_mean, running_var, save_mean, save_invstd};
-  return prenorm_common<float>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N, C,
-                               L, d, stream, false, &t);
+  return prenorm_common<float>(x, x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
+                               C, L, d, stream, false, Norm::Train, &t);
 }
 
 int prenorm_dconv1d_fwd_train_bf16(const uint16_t* x, float* running_mean, float* running_var,
@@ -296,8 +314,24 @@ int prenorm_dconv1d_fwd_train_bf16(const uint16_t* x, float* running_mean, float
                                    int64_t L, int64_t d, hipStream_t stream) {
   g_err.clear();
   const TrainBn t{momentum, running_mean, running_var, save_mean, save_invstd};
-  return prenorm_common<uint16_t>(x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
-                                  C, L, d, stream, true, &t);
+  return prenorm_common<uint16_t>(x, x, running_mean, running_var, gamma, beta, eps, W, b, out,
+                                  N, C, L, d, stream, true, Norm::Train, &t);
+}
+
+int relu_dconv1d_residual_fwd(const float* xn, const float* W, const float* b,
+                              const float* residual, float* out, int64_t N, int64_t C, int64_t L,
+                              int64_t d, hipStream_t stream) {
+  g_err.clear();
+  return prenorm_common<float>(xn, residual, nullptr, nullptr, nullptr, nullptr, 0.f, W, b, out,
+                               N, C, L, d, stream, false, Norm::External, nullptr);
+}
+
+int relu_dconv1d_residual_fwd_bf16(const uint16_t* xn, const float* W, const float* b,
+                                   const uint16_t* residual, uint16_t* out, int64_t N, int64_t C,
+                                   int64_t L, int64_t d, hipStream_t stream) {
+  g_err.clear();
+  return prenorm_common<uint16_t>(xn, residual, nullptr, nullptr, nullptr, nullptr, 0.f, W, b,
+                                  out, N, C, L, d, stream, true, Norm::External, nullptr);
 }
 
 int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, const float* gamma,

@@ -258,7 +258,10 @@ conv_bf16_kernel(ConvF32Args a) {
   }
 
   // Epilogue: register r of block (mb, nb) is channel 16mb + 4*lq + r, time 16nb + l16.
-  uint16_t* __restrict__ outn = reinterpret_cast<uint16_t*>(a.out) + (size_t)n * a.C_out * a.L_out;
+  // not restrict: the residual may be out itself (in-place residual add)
+  uint16_t* outn = reinterpret_cast<uint16_t*>(a.out) + (size_t)n * a.C_out * a.L_out;
+  const uint16_t* resn =
+      reinterpret_cast<const uint16_t*>(a.residual) + (size_t)n * a.C_out * a.L_out;
   const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
   // Residual and bias loads use clamped (always in-bounds) addresses and are issued a
   // 16-channel block at a time before any use, so each block pays the memory latency
@@ -274,7 +277,7 @@ conv_bf16_kernel(ConvF32Args a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int tc = min(t0 + 16 * nb + l16, a.L_out - 1);
-        res[r][nb] = xn[(size_t)coc * a.L_in + tc];
+        res[r][nb] = resn[(size_t)coc * a.L_out + tc];
       }
     }
 #pragma unroll
@@ -329,7 +332,9 @@ prep_bf16_kernel(const float* __restrict__ W, int C_out, int C_in, int NCB, int 
   }
   if (scale != nullptr && idx < Cin_pad) {
     float sc = 0.f, sh = 0.f;
-    if (idx < C_in) {
+    if (idx < C_in && gamma == nullptr) {
+      sc = 1.f;                          // no normalisation: the stage applies ReLU only
+    } else if (idx < C_in) {
       const double sd = (double)gamma[idx] / sqrt((double)var[idx] + (double)eps);
       sc = (float)sd;
       sh = (float)((double)beta[idx] - (double)mean[idx] * sd);

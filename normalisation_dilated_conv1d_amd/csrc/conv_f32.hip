@@ -219,9 +219,11 @@ conv_f32_kernel(ConvF32Args a) {
 
   // Epilogue. Accumulator register r of block (mb, nb) holds output channel
   // 16*mb + 4*lq + r (within the wave's 64) and time 16*nb + l16.
-  XT* __restrict__ outn = reinterpret_cast<XT*>(a.out) + (size_t)n * a.C_out * a.L_out;
+  // not restrict: the residual may be out itself (in-place residual add)
+  XT* outn = reinterpret_cast<XT*>(a.out) + (size_t)n * a.C_out * a.L_out;
   const int co_base = ct * CO_TILE + 16 * MB * w + 4 * lq;
   if (EPI == EPI_RESIDUAL) {
+    const XT* resn = reinterpret_cast<const XT*>(a.residual) + (size_t)n * a.C_out * a.L_out;
     // Residual and bias loads use clamped (always in-bounds) addresses and are issued
     // a 16-channel block at a time before any use, so each block pays the memory
     // latency once; only the stores are predicated.
@@ -235,8 +237,7 @@ conv_f32_kernel(ConvF32Args a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int tc = min(t0 + 16 * nb + l16, a.L_out - 1);
-          // residual: C_in == C_out and L_in == L_out for the block
-          res[r][nb] = to_f32(xn[coc * a.L_in + tc]);
+          res[r][nb] = to_f32(resn[coc * a.L_out + tc]);
         }
       }
 #pragma unroll

@@ -22,6 +22,9 @@ struct ConvF32Args {
   const float* Wp;       // repacked weights, see prep.hip
   const float* bias;     // [C_out] or nullptr
   void* out;             // [N][C_out][L_out], same storage type as x
+  const void* residual;  // [N][C_out][L_out], same storage type as out; added by the
+                         // residual epilogue (x for the block). May equal out exactly:
+                         // each element is read by the thread that then writes it.
   float* partials;       // GroupNorm: [N][C_out][n_tt][2] (tile sum, centred sum of squares)
   int N, C_in, C_out, L_in, L_out;
   int pad, dil;          // tap k reads input t - pad + k*dil

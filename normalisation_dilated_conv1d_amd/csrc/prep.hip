@@ -6,6 +6,8 @@
 //      shift[c] = beta[c] - running_mean[c] * scale[c]
 //    computed in double and rounded once to float, so the staged activation is
 //    ReLU(fma(x, scale, shift)). Channels in [C_in, Cin_pad) get scale = shift = 0.
+//    With gamma null (the caller normalised already) scale = 1 and shift = 0, so the
+//    stage computes ReLU(x) exactly; with scale null the fold is skipped.
 //
 // 2. Weight repack from PyTorch's [C_out][C_in][3] into the register order of the MFMA
 //    A operand (the first page's design turn proposes a transposed weight layout so the
@@ -52,7 +54,9 @@ prep_f32_kernel(const float* __restrict__ W, int C_out, int C_in, int NCB, int t
   }
   if (scale != nullptr && idx < Cin_pad) {
     float sc = 0.f, sh = 0.f;
-    if (idx < C_in) {
+    if (idx < C_in && gamma == nullptr) {
+      sc = 1.f;                          // no normalisation: the stage applies ReLU only
+    } else if (idx < C_in) {
       const double s = (double)gamma[idx] / sqrt((double)var[idx] + (double)eps);
       sc = (float)s;
       sh = (float)((double)beta[idx] - (double)mean[idx] * s);

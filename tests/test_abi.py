@@ -11,7 +11,8 @@ pytestmark = pytest.mark.skipif(not __import__("os").path.exists(dc.LIB_PATH),
                                 reason="libdconv1d.so not built")
 
 EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_bf16", "prenorm_dconv1d_fwd_train",
-            "prenorm_dconv1d_fwd_train_bf16", "conv1d_groupnorm_fwd",
+            "prenorm_dconv1d_fwd_train_bf16", "relu_dconv1d_residual_fwd",
+            "relu_dconv1d_residual_fwd_bf16", "conv1d_groupnorm_fwd",
             "dconv1d_last_error", "dconv1d_release", "dconv1d_timer_enable",
             "dconv1d_timer_read"}
 
@@ -90,6 +91,32 @@ def _train(lib, fn="prenorm_dconv1d_fwd_train", x=FAKE_X, out=FAKE_OUT, rm=FAKE_
 def test_train_validation(fn, kw, code):
     lib = dc.load_library()
     assert _train(lib, fn=fn, **kw) == code
+    if code != dc.DCONV1D_OK:
+        assert lib.dconv1d_last_error().decode()
+
+
+FAKE_RES = 0x50000000
+
+
+def _ext(lib, fn="relu_dconv1d_residual_fwd", xn=FAKE_X, res=FAKE_RES, out=FAKE_OUT, W=FAKE_P,
+         N=2, C=16, L=512, d=128):
+    return getattr(lib, fn)(xn, W, None, res, out, N, C, L, d, None)
+
+
+@pytest.mark.parametrize("fn", ["relu_dconv1d_residual_fwd", "relu_dconv1d_residual_fwd_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(xn=None), dc.DCONV1D_EINVAL), (dict(res=None), dc.DCONV1D_EINVAL),
+    (dict(out=None), dc.DCONV1D_EINVAL), (dict(W=None), dc.DCONV1D_EINVAL),
+    (dict(d=0), dc.DCONV1D_EINVAL), (dict(L=0), dc.DCONV1D_EINVAL),
+    (dict(out=FAKE_X + 64), dc.DCONV1D_EALIAS),           # out overlaps xn
+    (dict(out=FAKE_RES + 64), dc.DCONV1D_EALIAS),         # shifted view of residual
+    (dict(N=0), dc.DCONV1D_OK), (dict(N=0, xn=None, res=None, out=None), dc.DCONV1D_OK),
+    (dict(N=0, out=FAKE_RES), dc.DCONV1D_OK),             # in-place residual is allowed
+    (dict(N=0, res=FAKE_X), dc.DCONV1D_OK),               # residual may be xn
+])
+def test_external_bn_validation(fn, kw, code):
+    lib = dc.load_library()
+    assert _ext(lib, fn=fn, **kw) == code
     if code != dc.DCONV1D_OK:
         assert lib.dconv1d_last_error().decode()
 
