@@ -9,7 +9,10 @@ all inputs resident in HBM. Prints one JSON line.
                     [--workload 1|3|4]
 
 --workload 3 (Conv1d+GroupNorm) and 4 (bf16 storage) time the other workloads the same
-way; the default, workload 1, is the reported metric.
+way; the default, workload 1, is the reported metric. For the block workloads,
+--bn train times the training-mode entry point (batch-statistics pass, running-stat
+update, then the same conv) and --bn external the entry point that takes an already
+normalised input and a separate residual.
 """
 from __future__ import annotations
 
@@ -82,8 +85,13 @@ def main():
                     help="1: fp32 block N32 C256 L4096 d128 (default, the reported metric); "
                          "3: Conv1d+GroupNorm N16 Cin128 Cout256 T1024 G32; "
                          "4: bf16-storage block N16 C512 L16384 d128")
+    ap.add_argument("--bn", default="eval", choices=("eval", "train", "external"),
+                    help="block workloads: BatchNorm in eval mode (default), training mode, "
+                         "or done by the caller (ReLU + conv + separate residual)")
     args = ap.parse_args()
 
+    if args.bn != "eval" and args.workload == 3:
+        ap.error("--bn applies to the block workloads (1 and 4)")
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
               "supported (the block shards over the batch with no exchange, see the design "
@@ -106,19 +114,41 @@ def main():
         p = prenorm_inputs(N, C, L, seed_for(args.workload), bf16=bf16)
         q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
         out = torch.empty_like(q["x"])
-        fn = dc.prenorm_dconv1d_fwd_bf16 if bf16 else dc.prenorm_dconv1d_fwd
+        if args.bn == "eval":
+            fn = dc.prenorm_dconv1d_fwd_bf16 if bf16 else dc.prenorm_dconv1d_fwd
 
-        def step():
-            fn(q["x"], q["running_mean"], q["running_var"], q["gamma"], q["beta"], q["eps"],
-               q["W"], q["b"], d, out=out)
+            def step():
+                fn(q["x"], q["running_mean"], q["running_var"], q["gamma"], q["beta"], q["eps"],
+                   q["W"], q["b"], d, out=out)
+        elif args.bn == "train":
+            fn = dc.prenorm_dconv1d_fwd_train_bf16 if bf16 else dc.prenorm_dconv1d_fwd_train
+            rm, rv = q["running_mean"].clone(), q["running_var"].clone()
+            sm, si = torch.empty_like(rm), torch.empty_like(rm)
+
+            def step():
+                fn(q["x"], rm, rv, q["gamma"], q["beta"], q["eps"], 0.1, q["W"], q["b"], d,
+                   out=out, save_mean=sm, save_invstd=si)
+        else:
+            fn = dc.relu_dconv1d_residual_fwd_bf16 if bf16 else dc.relu_dconv1d_residual_fwd
+            # the caller's normalised activation, made once outside the timed region
+            xn = torch.nn.functional.batch_norm(
+                q["x"].float(), q["running_mean"], q["running_var"], q["gamma"], q["beta"],
+                training=False, eps=q["eps"]).to(q["x"].dtype).contiguous()
+
+            def step():
+                fn(xn, q["W"], q["b"], q["x"], d, out=out)
 
         C_in = C_out = C
         T_out = L
         esz = 2 if bf16 else 4
         flops = 2.0 * N * L * C * 3 * C
         alg_bytes = esz * 2.0 * N * C * L + 4.0 * (3 * C * C + 5 * C)
+        if args.bn != "eval":
+            # train: the statistics pass reads x before the conv can start; external: the
+            # normalised input and the residual are separate tensors
+            alg_bytes += esz * 1.0 * N * C * L
         config = {"workload": wl.name, "N": N, "C": C, "L": L, "kernel_size": 3,
-                  "dilation": d, "padding": d, "parallelism": "single GPU"}
+                  "dilation": d, "padding": d, "bn_mode": args.bn, "parallelism": "single GPU"}
         kernel_name = ("conv_bf16_kernel<pair>" if bf16
                        else "conv_f32_kernel<128, BN, residual, float>")
     else:
@@ -177,7 +207,9 @@ def main():
     gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
     k_tflops = flops / (kern_ms_avg * 1e-3) / 1e12
     metric = ("fused block TFLOP/s & GB/s (N32 C256 L4096 d128) vs MI355X roofline"
-              if args.workload == 1 else f"TFLOP/s & GB/s, {wl.name}, vs MI355X roofline")
+              if args.workload == 1 and args.bn == "eval"
+              else f"TFLOP/s & GB/s, {wl.name}, BN {args.bn}, vs MI355X roofline"
+              if wl.kind == "prenorm" else f"TFLOP/s & GB/s, {wl.name}, vs MI355X roofline")
 
     line = {
         "metric": metric,
@@ -198,13 +230,14 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(k_tflops, 3),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(k_tflops / peak, 4),
-                     "traffic": measured_traffic() if args.workload == 1 else None,
+                     "traffic": (measured_traffic()
+                                 if args.workload == 1 and args.bn == "eval" else None),
                      "kernel": kernel_name,
                      "kernel_ms": round(kern_ms_avg, 5),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": alg_bytes},
     }
-    if not args.no_cpu_baseline and args.workload == 1:
+    if not args.no_cpu_baseline and args.workload == 1 and args.bn == "eval":
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

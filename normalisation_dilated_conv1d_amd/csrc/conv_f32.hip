@@ -93,10 +93,12 @@ conv_f32_kernel(ConvF32Args a) {
   const int b = blockIdx.x;
   const int per = nwg >> 3, rem = nwg & 7, xcd = b & 7;
   const int logical = xcd * per + min(xcd, rem) + (b >> 3);
-  const int ct = logical % a.n_ct;
+  // the tile indices are wave-uniform: readfirstlane keeps them (and the addresses
+  // derived from them, such as the buffer resource of x) in scalar registers
+  const int ct = __builtin_amdgcn_readfirstlane(logical % a.n_ct);
   const int rest = logical / a.n_ct;
-  const int tt = rest % a.n_tt;
-  const int n = rest / a.n_tt;
+  const int tt = __builtin_amdgcn_readfirstlane(rest % a.n_tt);
+  const int n = __builtin_amdgcn_readfirstlane(rest / a.n_tt);
   const int t0 = tt * TT;
 
   const XT* __restrict__ xn = reinterpret_cast<const XT*>(a.x) + (size_t)n * a.C_in * a.L_in;
