@@ -111,7 +111,11 @@ conv_bf16_kernel(ConvF32Args a) {
   // per-lane time offset is one register per chunk, so a load costs no vector address
   // arithmetic (the weights stay plain global loads: that measured faster).
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(xn), (short)0, a.C_in * a.L_in * 2, kBufferFlags);
+      const_cast<uint16_t*>(xn), (short)0, (int)(2u * (uint32_t)a.C_in * (uint32_t)a.L_in),
+      kBufferFlags);
+  // Byte offsets within one sample's x: C_in*L_in < 2^31 (checked on the host), so
+  // 2*C_in*L_in fits 32 unsigned bits; the buffer takes them as raw 32-bit words.
+  auto row_bytes = [&](int ci) { return (int)(2u * (uint32_t)ci * (uint32_t)a.L_in); };
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
     const int off = k * a.dil - a.pad;
@@ -121,7 +125,7 @@ conv_bf16_kernel(ConvF32Args a) {
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
-        xr[i] = __builtin_amdgcn_raw_buffer_load_b32(xres, vo, ci * a.L_in * 2, 0);
+        xr[i] = __builtin_amdgcn_raw_buffer_load_b32(xres, vo, row_bytes(ci), 0);
       }
     } else {
 #pragma unroll
@@ -131,7 +135,7 @@ conv_bf16_kernel(ConvF32Args a) {
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
           const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
-          xr[j * RPW + i] = __builtin_amdgcn_raw_buffer_load_b16(xres, vo, ci * a.L_in * 2, 0);
+          xr[j * RPW + i] = __builtin_amdgcn_raw_buffer_load_b16(xres, vo, row_bytes(ci), 0);
         }
       }
     }

@@ -127,10 +127,11 @@ def prenorm_block_points(x, running_mean, running_var, gamma, beta, eps, W, b, d
 
     For each point: out = x[n, co, t] + b[co] + sum_k W[co, :, k] . z[n, :, t-d+k*d],
     where z = ReLU(BN_eval(x)) and a tap outside [0, L) contributes 0 (the zero padding
-    of the conv input). Used to check full-size runs on a sample of outputs.
+    of the conv input). Used to check full-size runs on a sample of outputs; x and W are
+    only indexed (one column of x and one row of W per tap), so they may be any array-like
+    that supports that, including tensors too large to upcast whole.
     """
     xs = x
-    W64 = _f64(W)
     b64 = None if b is None else _f64(b)
     rm, rv = _f64(running_mean), _f64(running_var)
     g, be = _f64(gamma), _f64(beta)
@@ -145,7 +146,7 @@ def prenorm_block_points(x, running_mean, running_var, gamma, beta, eps, W, b, d
                 col = _f64(xs[n, :, t_in])                      # all input channels
                 normalised = (col - rm) / np.sqrt(rv + float(eps))
                 z = np.maximum(g * normalised + be, 0.0)
-                acc += float(np.dot(W64[co, :, k], z))
+                acc += float(np.dot(_f64(W[co, :, k]), z))      # one row of W at a time
         out[i] = float(_f64(xs[n, co, t])) + acc
     return out
 
