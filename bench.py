@@ -46,6 +46,17 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, min_seconds: float):
     """The float64 oracle, untuned, on the host cores: repeats the whole workload until
     at least `min_seconds` have passed (at least once)."""
@@ -65,11 +76,15 @@ def cpu_baseline(w, min_seconds: float):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                             for i in info if i.get("user_api") == "blas"})) or "unknown"
     return {"value": round(flops * reps / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"whole N=32 C=256 L=4096 d=128 workload, float64 numpy oracle, "
-                      f"{reps} run(s) in {el:.1f} s"}
+                      f"{reps} run(s) in {el:.1f} s",
+            "cpu": cpu_model(), "blas": blas}
 
 
 def main():
@@ -186,6 +201,28 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / args.steps
 
+    # per-step durations (median), warm and with the MALL flushed: before each cold step a
+    # 512 MiB scratch buffer is overwritten, so x (134 MB for the default workload) does
+    # not stay resident in the 256 MB last-level cache between steps
+    def per_step_ms(flush):
+        scratch = torch.empty(512 * (1 << 20) // 4, device=dev) if flush else None
+        times = []
+        for i in range(args.steps):
+            if flush:
+                scratch.fill_(float(i))
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            step()
+            b_ev.record(stream)
+            times.append((a_ev, b_ev))
+        torch.cuda.synchronize()
+        ms = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in times)
+        del scratch
+        return ms[len(ms) // 2]
+
+    warm_median = per_step_ms(False)
+    cold_median = per_step_ms(True)
+
     # dominant kernel alone: HIP events recorded by the library around each launch of
     # the fused conv kernel, on the stream it is launched on
     with dc.KernelTimer() as kt:
@@ -226,6 +263,8 @@ def main():
         "data": "synthetic",
         "config": config,
         "hbm_gbps_algorithmic": round(gbps, 2),
+        "ms_per_step_median": round(warm_median, 5),
+        "ms_per_step_median_cold_mall": round(cold_median, 5),
         "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(k_tflops, 3),
                      "peak": peak, "unit": "TFLOP/s",

@@ -12,6 +12,14 @@
         device-to-device copy of --calib-mib MiB in the same run (expected: that many MiB
         read and written), and the record carries the SHA-256 of the kernel's sources so a
         reader can tell when it no longer describes the current kernel.
+
+    python -m normalisation_dilated_conv1d_amd.profiling mfma COUNTER_CSV --kernel conv_f32_kernel \
+        --algorithmic-flops F --cmd "..."
+        Executed MFMA work and MFMA-pipe utilisation per launch of one kernel from a
+        ``rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_<type> SQ_VALU_MFMA_BUSY_CYCLES
+        GRBM_GUI_ACTIVE`` run: flops = MOPS * 512; utilisation = busy cycles /
+        (per-XCD active cycles * SIMDs), where the reported GRBM_GUI_ACTIVE is the sum
+        over the 8 XCDs and the part has 1024 SIMDs.
 """
 from __future__ import annotations
 
@@ -105,6 +113,37 @@ def traffic_record(fetch_csv, write_csv, kernel, calib_mib, cmd_fetch, cmd_write
     }
 
 
+N_XCD = 8
+N_SIMD = 1024
+
+
+def mfma_markdown(path, kernel, alg_flops, cmd):
+    rows = _counter_rows(path)
+    per = {}
+    for r in rows:
+        if kernel not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                              "us": (int(r["End_Timestamp"]) -
+                                                     int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"kernel {kernel} not found in counter output")
+    out = ["| dispatch | executed MFMA flops | / algorithmic | MFMA busy cycles | "
+           "active cycles per XCD | MFMA utilisation | duration under the profiler (us) |",
+           "|---|---|---|---|---|---|---|"]
+    for did, d in sorted(per.items(), key=lambda kv: int(kv[0])):
+        mops = sum(v for k, v in d.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
+        flops = mops * 512
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        active = d.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        util = busy / (active * N_SIMD) if active else float("nan")
+        out.append(f"| {did} | {flops:.4g} | {flops / alg_flops:.4f} | {busy:.4g} | {active:.4g} | "
+                   f"{100 * util:.1f}% | {d['us']:.1f} |")
+    name = next(iter(per.values()))["name"]
+    return (f"Kernel: `{name}`\n\nCommand:\n\n```\n{cmd}\n```\n\n" + "\n".join(out) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -119,9 +158,16 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--algorithmic-flops", type=float, required=True)
+    m.add_argument("--cmd", required=True)
     a = ap.parse_args(argv)
     if a.what == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.cmd))
+    elif a.what == "mfma":
+        sys.stdout.write(mfma_markdown(a.csv, a.kernel, a.algorithmic_flops, a.cmd))
     else:
         rec = traffic_record(a.fetch, a.write, a.kernel, a.calib_mib, a.cmd_fetch, a.cmd_write)
         with open(a.out, "w") as f:
