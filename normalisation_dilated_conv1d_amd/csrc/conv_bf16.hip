@@ -269,32 +269,93 @@ conv_bf16_kernel(ConvF32Args a) {
   const uint16_t* resn =
       reinterpret_cast<const uint16_t*>(a.residual) + (size_t)n * a.C_out * a.L_out;
   const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
-  // Residual and bias loads use clamped (always in-bounds) addresses and are issued a
-  // 16-channel block at a time before any use, so each block pays the memory latency
-  // once; only the stores are predicated.
+  const bool vec_epi = ((a.L_out & 7) == 0) &&
+                       (((reinterpret_cast<uintptr_t>(a.out) |
+                          reinterpret_cast<uintptr_t>(a.residual)) & 15) == 0);
+  if (vec_epi) {
+    // Each 16-channel block of accumulators goes through LDS (the staging buffers are
+    // idle: the main loop ended with a barrier) so that a lane then owns 8 consecutive
+    // time steps of one channel: one 16-byte residual load and one 16-byte store per 8
+    // outputs instead of eight 2-byte ones. Every wave uses its own 16 x (128+4) float
+    // tile; the LDS accesses of a wave complete in order, so it needs no barrier.
+    constexpr int EP = TTB + 4;
+    float* ep = reinterpret_cast<float*>(&zs[0][0]) + w * (16 * EP);
+    const int co_w = ct * CO_TILE_F32 + 64 * w;
+    // after the transpose, lane (lq, l16) holds rows lq + 4i (i = 0..3) of each block,
+    // time steps t0 + 8*l16 .. +7
+    float bia[4][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    uint16_t res[4][NB];
-    float bco[4];
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int coc = min(co_base + 16 * mb + r, a.C_out - 1);
-      bco[r] = a.bias ? a.bias[coc] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int coc = min(co_w + 16 * mb + lq + 4 * i, a.C_out - 1);
+        bia[mb][i] = a.bias ? a.bias[coc] : 0.f;
+      }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int tc = min(t0 + 16 * nb + l16, a.L_out - 1);
-        res[r][nb] = resn[(size_t)coc * a.L_out + tc];
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) ep[(4 * lq + r) * EP + 16 * nb + l16] = acc[mb][nb][r];
+      // residual loads (clamped in-bounds; L_out is a multiple of 8, so a clamped start
+      // is too) go out before any use
+      u32x4 rv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int coc = min(co_w + 16 * mb + lq + 4 * i, a.C_out - 1);
+        const int tcl = min(t0 + 8 * l16, a.L_out - 8);
+        rv[i] = *reinterpret_cast<const u32x4*>(resn + (size_t)coc * a.L_out + tcl);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = lq + 4 * i;
+        const int co = co_w + 16 * mb + row;
+        const int t = t0 + 8 * l16;
+        const float* src = ep + row * EP + 8 * l16;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 o = {v[2 * e] + bia[mb][i] + bf16_lo(rv[i][e]),
+                           v[2 * e + 1] + bia[mb][i] + bf16_hi(rv[i][e])};
+          pk[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2));
+        }
+        const u32x4 ov = {pk[0], pk[1], pk[2], pk[3]};
+        // t and L_out are multiples of 8: the 8 steps are all in range or all out
+        if (co < a.C_out && t < a.L_out)
+          *reinterpret_cast<u32x4*>(outn + (size_t)co * a.L_out + t) = ov;
       }
     }
+  } else {
+    // Residual and bias loads use clamped (always in-bounds) addresses and are issued a
+    // 16-channel block at a time before any use, so each block pays the memory latency
+    // once; only the stores are predicated.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int co = co_base + 16 * mb + r;
+    for (int mb = 0; mb < 4; ++mb) {
+      uint16_t res[4][NB];
+      float bco[4];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int t = t0 + 16 * nb + l16;
-        if (co < a.C_out && t < a.L_out) {
-          const float o = acc[mb][nb][r] + bco[r] + bf16_to_f32(res[r][nb]);
-          outn[(size_t)co * a.L_out + t] = __builtin_bit_cast(uint16_t, (__bf16)o);
+      for (int r = 0; r < 4; ++r) {
+        const int coc = min(co_base + 16 * mb + r, a.C_out - 1);
+        bco[r] = a.bias ? a.bias[coc] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int tc = min(t0 + 16 * nb + l16, a.L_out - 1);
+          res[r][nb] = resn[(size_t)coc * a.L_out + tc];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int co = co_base + 16 * mb + r;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int t = t0 + 16 * nb + l16;
+          if (co < a.C_out && t < a.L_out) {
+            const float o = acc[mb][nb][r] + bco[r] + bf16_to_f32(res[r][nb]);
+            outn[(size_t)co * a.L_out + t] = __builtin_bit_cast(uint16_t, (__bf16)o);
+          }
         }
       }
     }
