@@ -226,6 +226,55 @@ conv_f32_kernel(ConvF32Args a) {
   const int co_base = ct * CO_TILE + 16 * MB * w + 4 * lq;
   if (EPI == EPI_RESIDUAL) {
     const XT* resn = reinterpret_cast<const XT*>(a.residual) + (size_t)n * a.C_out * a.L_out;
+    const bool vec_epi = sizeof(XT) == 4 && ((a.L_out & 3) == 0) &&
+                         (((reinterpret_cast<uintptr_t>(a.out) |
+                            reinterpret_cast<uintptr_t>(a.residual)) & 15) == 0);
+    if (vec_epi) {
+      // Each 16-channel block of accumulators goes through LDS (the staging buffers are
+      // idle: the main loop ended with a barrier) so that a lane then owns 4 consecutive
+      // time steps of one channel: 16-byte residual loads and stores. Every wave uses
+      // its own 16 x (TT+4) float tile; the LDS accesses of a wave complete in order, so
+      // it needs no barrier.
+      constexpr int EP = TT + 4;
+      constexpr int CH = TT / 4;              // float4 chunks per row
+      constexpr int IPL = 16 * CH / 64;       // (row, chunk) items per lane per block
+      float* ep = &zs[0][0] + w * (16 * EP);
+      const int co_w = ct * CO_TILE + 16 * MB * w;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) ep[(4 * lq + r) * EP + 16 * nb + l16] = acc[mb][nb][r];
+        // residual and bias loads (clamped in-bounds; L_out is a multiple of 4, so a
+        // clamped chunk start is too) go out before any use
+        f32x4 rv[IPL];
+        float bia[IPL];
+#pragma unroll
+        for (int i = 0; i < IPL; ++i) {
+          const int item = l + 64 * i;
+          const int row = item / CH, ch = item % CH;
+          const int coc = min(co_w + 16 * mb + row, a.C_out - 1);
+          const int tcl = min(t0 + 4 * ch, a.L_out - 4);
+          rv[i] = *reinterpret_cast<const f32x4*>(resn + (size_t)coc * a.L_out + tcl);
+          bia[i] = a.bias ? a.bias[coc] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < IPL; ++i) {
+          const int item = l + 64 * i;
+          const int row = item / CH, ch = item % CH;
+          const int co = co_w + 16 * mb + row;
+          const int t = t0 + 4 * ch;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ep + row * EP + 4 * ch);
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = v[e] + bia[i] + rv[i][e];
+          // t and L_out are multiples of 4: the 4 steps are all in range or all out
+          if (co < a.C_out && t < a.L_out)
+            *reinterpret_cast<f32x4*>(outn + (size_t)co * a.L_out + t) = o;
+        }
+      }
+    } else
     // Residual and bias loads use clamped (always in-bounds) addresses and are issued
     // a 16-channel block at a time before any use, so each block pays the memory
     // latency once; only the stores are predicated.
