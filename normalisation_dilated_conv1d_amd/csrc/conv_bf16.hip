@@ -273,11 +273,14 @@ conv_bf16_kernel(ConvF32Args a) {
                        (((reinterpret_cast<uintptr_t>(a.out) |
                           reinterpret_cast<uintptr_t>(a.residual)) & 15) == 0);
   if (vec_epi) {
-    // Each 16-channel block of accumulators goes through LDS (the staging buffers are
-    // idle: the main loop ended with a barrier) so that a lane then owns 8 consecutive
-    // time steps of one channel: one 16-byte residual load and one 16-byte store per 8
-    // outputs instead of eight 2-byte ones. Every wave uses its own 16 x (128+4) float
-    // tile; the LDS accesses of a wave complete in order, so it needs no barrier.
+    // Each 16-channel block of accumulators goes through the staging LDS so that a lane
+    // then owns 8 consecutive time steps of one channel: one 16-byte residual load and
+    // one 16-byte store per 8 outputs instead of eight 2-byte ones. The loop ends with a
+    // barrier (the chunk count is even), so every wave is done with the B operands; the
+    // explicit one keeps that true should the loop change. Every wave uses its own
+    // 16 x (128+4) float tile; the LDS accesses of a wave complete in order, so no
+    // further barrier is needed.
+    __syncthreads();
     constexpr int EP = TTB + 4;
     float* ep = reinterpret_cast<float*>(&zs[0][0]) + w * (16 * EP);
     const int co_w = ct * CO_TILE_F32 + 64 * w;

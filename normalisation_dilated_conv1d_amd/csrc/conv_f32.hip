@@ -230,11 +230,13 @@ conv_f32_kernel(ConvF32Args a) {
                          (((reinterpret_cast<uintptr_t>(a.out) |
                             reinterpret_cast<uintptr_t>(a.residual)) & 15) == 0);
     if (vec_epi) {
-      // Each 16-channel block of accumulators goes through LDS (the staging buffers are
-      // idle: the main loop ended with a barrier) so that a lane then owns 4 consecutive
-      // time steps of one channel: 16-byte residual loads and stores. Every wave uses
-      // its own 16 x (TT+4) float tile; the LDS accesses of a wave complete in order, so
-      // it needs no barrier.
+      // Each 16-channel block of accumulators goes through the staging LDS so that a
+      // lane then owns 4 consecutive time steps of one channel: 16-byte residual loads
+      // and stores. The barrier makes sure every wave has finished reading its last B
+      // operands (with an odd chunk count the loop ends without one). Every wave then
+      // uses its own 16 x (TT+4) float tile; the LDS accesses of a wave complete in
+      // order, so no further barrier is needed.
+      __syncthreads();
       constexpr int EP = TT + 4;
       constexpr int CH = TT / 4;              // float4 chunks per row
       constexpr int IPL = 16 * CH / 64;       // (row, chunk) items per lane per block

@@ -96,6 +96,11 @@ BLOCK_CASES = [
     (8, 64, 8200, 128),      # 128-wide time tiles with a ragged tail
     (2, 33, 257, 31),
     (8, 64, 5000, 77),       # 64-step x 256-channel tiles
+    # odd chunk counts (C_in padded to 32 or 96: 3 or 9 chunks) with L % 4 == 0, where the
+    # main loop ends without a barrier before the LDS-transposed epilogue
+    (4, 96, 2048, 3),
+    (6, 32, 4096, 64),
+    (3, 16, 1024, 5),
 ]
 
 
@@ -218,6 +223,8 @@ GN_CASES = [
     (4, 128, 256, 1023, 32, 1, 1, False, True),  # ragged time tail
     (8, 32, 64, 5000, 8, 1, 1, True, True),      # 64-step x 256-channel tiles
     (2, 64, 300, 150, 3, 1, 1, False, True),     # 128-channel tiles, 3 channel tiles
+    (2, 96, 128, 2048, 8, 1, 1, True, True),     # 9 chunks (odd), T_out % 4 == 0
+    (4, 32, 256, 1026, 16, 0, 1, False, True),   # 3 chunks (odd), T_out = 1024
 ]
 
 
