@@ -47,5 +47,27 @@ def build_library(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "dconv1d_client.c")
+C_CLIENT_BIN = os.path.join(ROOT, "tests", "c_client", "dconv1d_client")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile the plain C client of the ABI (tests/c_client) with gcc against the built
+    library; it is run by the GPU tests."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [os.environ.get("CC", "gcc"), "-std=c99", "-O2", "-Wall", "-Wextra",
+           "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}", f"-I{rocm}/include", C_CLIENT_SRC,
+           f"-L{PKG}", "-ldconv1d", f"-L{rocm}/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../normalisation_dilated_conv1d_amd",
+           f"-Wl,-rpath,{rocm}/lib", "-o", C_CLIENT_BIN]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0 or res.stderr.strip():
+        raise RuntimeError(f"C client build failed ({res.returncode}):\n{res.stderr}")
+    return C_CLIENT_BIN
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_c_client(verbose=True))
