@@ -21,8 +21,11 @@
 //                order: one 16-byte load per (K-step, 16-channel block) per lane, loaded
 //                two K-steps ahead through a 4-slot register ring.
 //   x loads    = buffer loads (row offset in an SGPR). When every tap offset and L are
-//                even, each lane loads two adjacent time steps with one aligned 4-byte
-//                load; otherwise two 2-byte loads.
+//                even (the paired path), each lane loads two adjacent time steps with one
+//                aligned 4-byte load, and the loads go straight into LDS (buffer->LDS
+//                loads) two chunks ahead of their use, so x latency has two chunks to
+//                hide in and no staging registers are held across the MFMAs; otherwise
+//                two 2-byte loads into registers, one chunk ahead.
 //
 // K-slot mapping: in K-step s of a chunk, quarter-wave q = lane/16 element e (0..7) is
 // chunk row 32s + 8q + e, for A and B alike, so the sum over K is the plain sum over
@@ -69,7 +72,18 @@ conv_bf16_kernel(ConvF32Args a) {
   constexpr int NB = TTB / 16;              // 16-column MFMA blocks per wave (8)
   constexpr int RPW = KCB / 4;              // staged rows per wave (16)
   constexpr int PITCH = KCB + 8;            // bf16 per LDS column (144 bytes)
-  __shared__ __attribute__((aligned(16))) uint16_t zs[2][TTB * PITCH];
+  // Staged activations, double-buffered. Two separate arrays (not one 2-D one) and, for
+  // the paired path, two raw-x arrays: every LDS access below names its array directly,
+  // so the compiler can tell them apart and, before reading or writing one of them, waits
+  // only for the buffer->LDS loads into that same array, leaving the prefetch of the
+  // other one in flight.
+  __shared__ __attribute__((aligned(16))) uint16_t zsA[TTB * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t zsB[TTB * PITCH];
+  // Paired path: the raw x rows (64 channels x 128 steps) of the chunks one and two
+  // ahead; every wave fills and reads only its own 16 rows.
+  constexpr int RAWN = PAIR ? KCB * TTB : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t raw0[RAWN];
+  __shared__ __attribute__((aligned(16))) uint16_t raw1[RAWN];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,6 +130,20 @@ conv_bf16_kernel(ConvF32Args a) {
   // Byte offsets within one sample's x: C_in*L_in < 2^31 (checked on the host), so
   // 2*C_in*L_in fits 32 unsigned bits; the buffer takes them as raw 32-bit words.
   auto row_bytes = [&](int ci) { return (int)(2u * (uint32_t)ci * (uint32_t)a.L_in); };
+  auto load_bn = [&](int q) {
+    const int c = q / 3;
+    // wave-uniform addresses: read through the constant address space so the
+    // compiler issues scalar loads into SGPRs
+    const __attribute__((address_space(4))) float* scp =
+        (const __attribute__((address_space(4))) float*)(a.scale + c * KCB + RPW * w);
+    const __attribute__((address_space(4))) float* shp =
+        (const __attribute__((address_space(4))) float*)(a.shift + c * KCB + RPW * w);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      sc[i] = scp[i];
+      sh[i] = shp[i];
+    }
+  };
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
     const int off = k * a.dil - a.pad;
@@ -139,17 +167,45 @@ conv_bf16_kernel(ConvF32Args a) {
         }
       }
     }
-    // wave-uniform addresses: read through the constant address space so the
-    // compiler issues scalar loads into SGPRs
-    const __attribute__((address_space(4))) float* scp =
-        (const __attribute__((address_space(4))) float*)(a.scale + c * KCB + RPW * w);
-    const __attribute__((address_space(4))) float* shp =
-        (const __attribute__((address_space(4))) float*)(a.shift + c * KCB + RPW * w);
+    load_bn(q);
+  };
+  // Paired path: chunk q's raw x rows of this wave, one row of 128 steps per load (64
+  // lanes x 4 bytes), straight into LDS.
+  auto dma_x0 = [&](int q) {
+    const int c = q / 3, k = q - 3 * c;
+    const int ts = t0 + 2 * l + k * a.dil - a.pad;
+    const int vo = 2 * min(max(ts, 0), a.L_in - 2);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      sc[i] = scp[i];
-      sh[i] = shp[i];
+      const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)&raw0[(RPW * w + i) * TTB], 4, vo,
+          row_bytes(ci), 0, 0);
     }
+  };
+  auto dma_x1 = [&](int q) {
+    const int c = q / 3, k = q - 3 * c;
+    const int ts = t0 + 2 * l + k * a.dil - a.pad;
+    const int vo = 2 * min(max(ts, 0), a.L_in - 2);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)&raw1[(RPW * w + i) * TTB], 4, vo,
+          row_bytes(ci), 0, 0);
+    }
+  };
+  // (one copy of the buffer->LDS load and of the read per raw array, so each access
+  // names its array)
+  auto read_raw0 = [&] {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      xr[i] = *reinterpret_cast<const uint32_t*>(&raw0[(RPW * w + i) * TTB + 2 * l]);
+  };
+  auto read_raw1 = [&] {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      xr[i] = *reinterpret_cast<const uint32_t*>(&raw1[(RPW * w + i) * TTB + 2 * l]);
   };
   // z = ReLU(scale*x + shift) in float32, rounded to bf16 by the hardware pack (round to
   // nearest even), exactly 0 in the time padding; 8 consecutive rows of one column go to
@@ -218,7 +274,7 @@ conv_bf16_kernel(ConvF32Args a) {
 
   // One chunk (two K-steps) on LDS buffer zb. `next` stages the next chunk into the
   // other buffer after the chunk's MFMAs, the latest point before the barrier, which
-  // gives its x loads (issued at the chunk's start) the longest time to arrive.
+  // gives its x loads the longest time to arrive.
   auto compute = [&](const uint16_t* zb, int q, auto P, auto&& next) {
     constexpr int par = decltype(P)::value;
 #pragma unroll
@@ -248,19 +304,55 @@ conv_bf16_kernel(ConvF32Args a) {
   const int Q = a.Q;
 #pragma unroll
   for (int S = 0; S < DIST; ++S) load_w(S, wr[S]);
-  load_x(0);
-  store_z(0, zs[0]);
-  __syncthreads();
-  for (int q = 0; q < Q; q += 2) {
-    load_x(q + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(zs[0], q, Parity<0>{}, [&] { store_z(q + 1, zs[1]); });
+  if constexpr (PAIR) {
+    // Chunk q: start the buffer->LDS loads of chunk q+2 (into the raw array chunk q was
+    // staged from), run chunk q's MFMAs, then stage chunk q+1 from the other raw array
+    // (loaded during chunk q-1). The barrier carries no memory fence: the release fence
+    // of __syncthreads would wait for the chunk q+2 loads still in flight. Nothing needs
+    // it: raw rows are read only by the wave that loaded them (the compiler waits for its
+    // own loads before the read), and the staged z writes are complete once lgkmcnt is 0.
+    // The memory clobber keeps the compiler from moving LDS accesses across it.
+    auto bar = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    dma_x0(0);
+    dma_x1(min(1, Q - 1));
+    load_bn(0);
+    read_raw0();
+    store_z(0, zsA);
+    bar();
+    for (int q = 0; q < Q; q += 2) {
+      dma_x0(min(q + 2, Q - 1));
+      load_bn(q + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(zsA, q, Parity<0>{}, [&] {
+        read_raw1();
+        store_z(q + 1, zsB);
+      });
+      bar();
+      const int qn = min(q + 2, Q - 1);
+      dma_x1(min(q + 3, Q - 1));
+      load_bn(qn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(zsB, q + 1, Parity<1>{}, [&] {
+        read_raw0();
+        store_z(qn, zsA);
+      });
+      bar();
+    }
+  } else {
+    load_x(0);
+    store_z(0, zsA);
     __syncthreads();
-    const int qn = min(q + 2, Q - 1);
-    load_x(qn);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(zs[1], q + 1, Parity<1>{}, [&] { store_z(qn, zs[0]); });
-    __syncthreads();
+    for (int q = 0; q < Q; q += 2) {
+      load_x(q + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(zsA, q, Parity<0>{}, [&] { store_z(q + 1, zsB); });
+      __syncthreads();
+      const int qn = min(q + 2, Q - 1);
+      load_x(qn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(zsB, q + 1, Parity<1>{}, [&] { store_z(qn, zsA); });
+      __syncthreads();
+    }
   }
 
   // Epilogue: register r of block (mb, nb) is channel 16mb + 4*lq + r, time 16nb + l16.
@@ -282,7 +374,8 @@ conv_bf16_kernel(ConvF32Args a) {
     // further barrier is needed.
     __syncthreads();
     constexpr int EP = TTB + 4;
-    float* ep = reinterpret_cast<float*>(&zs[0][0]) + w * (16 * EP);
+    // two 16 x (128+4) float tiles (16.9 KB) fit in each 18.4 KB staging buffer
+    float* ep = reinterpret_cast<float*>(w < 2 ? &zsA[0] : &zsB[0]) + (w & 1) * (16 * EP);
     const int co_w = ct * CO_TILE_F32 + 64 * w;
     // after the transpose, lane (lq, l16) holds rows lq + 4i (i = 0..3) of each block,
     // time steps t0 + 8*l16 .. +7
