@@ -108,9 +108,9 @@ def main():
     if args.bn != "eval" and args.workload == 3:
         ap.error("--bn applies to the block workloads (1 and 4)")
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
-              "supported (the block shards over the batch with no exchange, see the design "
-              "notes)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (the "
+              "block would shard over the batch with no exchange between GPUs)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
