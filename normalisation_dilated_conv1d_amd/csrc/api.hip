@@ -198,9 +198,12 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
 
   const int Ci = (int)C, Li = (int)L;
   // bf16 storage runs the bf16-MFMA kernel: 64-channel K-chunks, 128-step time tiles
+  // (a 256- or 512-channel tile), float32 the tile conv_f32_tile picks; the repacked
+  // weights are padded to whole channel tiles
   const int Cin_pad = round_up(Ci, bf16 ? CIN_PAD_BF16 : KC);
-  const int Cout_pad = round_up(Ci, CO_TILE_F32);
-  const ConvTile tile = bf16 ? ConvTile{TILE_T_BF16, 4}
+  const int co_tile_bf16 = bf16 ? conv_bf16_co_tile(N, Li, Ci) : 0;
+  const int Cout_pad = round_up(Ci, bf16 ? co_tile_bf16 : CO_TILE_F32);
+  const ConvTile tile = bf16 ? ConvTile{TILE_T_BF16, co_tile_bf16 / 64}
                              : conv_f32_tile(Li, (int)std::min<int64_t>(N, kMaxIndex), Ci);
   const int n_ct = (Ci + tile.co_tile() - 1) / tile.co_tile();
   const int n_tt = (Li + tile.tt - 1) / tile.tt;
@@ -268,7 +271,8 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   a.n_tt = n_tt;
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
-  e = bf16 ? launch_conv_bf16(a, stream) : launch_conv_f32(a, tile, EPI_RESIDUAL, stream);
+  e = bf16 ? launch_conv_bf16(a, tile.co_tile(), stream)
+           : launch_conv_f32(a, tile, EPI_RESIDUAL, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
   return DCONV1D_OK;

@@ -2,10 +2,12 @@
 // x and out (POPCORNBENCH "Kimi-K2.6__l2_p12", first turn: block definition, eval-mode
 // BN per channel, zero padding of the conv input, residual add).
 //
-// Same GEMM view and work split as the float32 kernel (conv_f32.hip): one workgroup per
-// (sample, 256 output channels, 128 time steps), 4 waves of 64 channels x 128 steps,
-// activations through LDS, weights straight from global memory into registers. What
-// changes for bfloat16:
+// Same GEMM view as the float32 kernel (conv_f32.hip): one workgroup per (sample, output
+// channel tile, 128 time steps), one wave per 64 channels x 128 steps, activations
+// through LDS, weights straight from global memory into registers. The channel tile is
+// 256 (4 waves) or, for wide layers, 512 (8 waves): every wave of a workgroup reads the
+// same staged activations, so the wider tile stages each x chunk once for twice the
+// MFMA work and halves the staging each wave does. What changes for bfloat16:
 //
 //   MFMA       = v_mfma_f32_16x16x32_bf16: 16x16 output block, K = 32 per instruction,
 //                float32 accumulation. A lane feeds 8 consecutive K values of one row
@@ -66,11 +68,15 @@ constexpr int KCB = 64;   // channel rows per chunk (two MFMA K-steps)
 constexpr int kBufferFlags = 0x00020000;
 constexpr int TTB = TILE_T_BF16;  // time steps per workgroup
 
-template <bool PAIR>
-__global__ void __launch_bounds__(NTHREADS, 2)
+// WV waves (4 or 8) per workgroup, two waves per SIMD (at most 256 registers each)
+template <bool PAIR, int WV>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
+                               amdgpu_waves_per_eu(2, 2)))
 conv_bf16_kernel(ConvF32Args a) {
+  static_assert(WV == 4 || WV == 8, "4 or 8 waves");
   constexpr int NB = TTB / 16;              // 16-column MFMA blocks per wave (8)
-  constexpr int RPW = KCB / 4;              // staged rows per wave (16)
+  constexpr int RPW = KCB / WV;             // staged rows per wave (16 or 8)
+  constexpr int CO_T = 64 * WV;             // output channels per workgroup
   constexpr int PITCH = KCB + 8;            // bf16 per LDS column (144 bytes)
   // Staged activations, double-buffered. Two separate arrays (not one 2-D one) and, for
   // the paired path, two raw-x arrays: every LDS access below names its array directly,
@@ -80,8 +86,12 @@ conv_bf16_kernel(ConvF32Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t zsA[TTB * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t zsB[TTB * PITCH];
   // Paired path: the raw x rows (64 channels x 128 steps) of the chunks one and two
-  // ahead; every wave fills and reads only its own 16 rows.
-  constexpr int RAWN = PAIR ? KCB * TTB : 2;
+  // ahead; every wave fills and reads only its own RPW rows. With 8 waves the two raw
+  // arrays also hold epilogue tiles of waves 4..7 (two 16 x (128+4) float tiles each),
+  // so they are at least that large on both paths.
+  constexpr int EP_TILE = 16 * (TTB + 4) * 2;     // one wave's epilogue tile, in uint16
+  constexpr int RAW_X = PAIR ? KCB * TTB : 2;
+  constexpr int RAWN = WV > 4 && 2 * EP_TILE > RAW_X ? 2 * EP_TILE : RAW_X;
   __shared__ __attribute__((aligned(16))) uint16_t raw0[RAWN];
   __shared__ __attribute__((aligned(16))) uint16_t raw1[RAWN];
 
@@ -106,7 +116,7 @@ conv_bf16_kernel(ConvF32Args a) {
   const uint16_t* __restrict__ xn =
       reinterpret_cast<const uint16_t*>(a.x) + (size_t)n * a.C_in * a.L_in;
   const u32x4* __restrict__ Wp4 = reinterpret_cast<const u32x4*>(a.Wp);
-  const int cb0 = (ct * CO_TILE_F32) / 16 + 4 * w;
+  const int cb0 = (ct * CO_T) / 16 + 4 * w;
 
   f32x4 acc[4][NB];
 #pragma unroll
@@ -116,7 +126,7 @@ conv_bf16_kernel(ConvF32Args a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[mb][nb][r] = 0.f;
 
-  // Staging: wave w stages rows [16w, 16w + 16) of the chunk. PAIR: lane l covers columns
+  // Staging: wave w stages rows [RPW*w, RPW*w + RPW) of the chunk. PAIR: lane l covers columns
   // 2l and 2l+1 with one 4-byte load per row; otherwise columns l and l + 64, 2 bytes each.
   uint32_t xr[RPW * (PAIR ? 1 : 2)];
   float sc[RPW], sh[RPW];
@@ -214,7 +224,7 @@ conv_bf16_kernel(ConvF32Args a) {
   // and shift are 0, so z = max(0*x + 0, 0) = 0 for the (finite) clamped load.
   auto stage_column = [&](auto&& get, int col, uint32_t tkeep, uint16_t* dst) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < RPW / 8; ++half) {
       uint32_t packed[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -360,7 +370,7 @@ conv_bf16_kernel(ConvF32Args a) {
   uint16_t* outn = reinterpret_cast<uint16_t*>(a.out) + (size_t)n * a.C_out * a.L_out;
   const uint16_t* resn =
       reinterpret_cast<const uint16_t*>(a.residual) + (size_t)n * a.C_out * a.L_out;
-  const int co_base = ct * CO_TILE_F32 + 64 * w + 4 * lq;
+  const int co_base = ct * CO_T + 64 * w + 4 * lq;
   const bool vec_epi = ((a.L_out & 7) == 0) &&
                        (((reinterpret_cast<uintptr_t>(a.out) |
                           reinterpret_cast<uintptr_t>(a.residual)) & 15) == 0);
@@ -369,14 +379,18 @@ conv_bf16_kernel(ConvF32Args a) {
     // then owns 8 consecutive time steps of one channel: one 16-byte residual load and
     // one 16-byte store per 8 outputs instead of eight 2-byte ones. The loop ends with a
     // barrier (the chunk count is even), so every wave is done with the B operands; the
-    // explicit one keeps that true should the loop change. Every wave uses its own
-    // 16 x (128+4) float tile; the LDS accesses of a wave complete in order, so no
-    // further barrier is needed.
+    // explicit one keeps that true should the loop change. The last trip's buffer->LDS
+    // load into raw1 is never read: the wait before the barrier lets it land before
+    // waves 6 and 7 put their tiles there. Every wave uses its own 16 x (128+4) float
+    // tile; the LDS accesses of a wave complete in order, so no further barrier is needed.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     constexpr int EP = TTB + 4;
-    // two 16 x (128+4) float tiles (16.9 KB) fit in each 18.4 KB staging buffer
-    float* ep = reinterpret_cast<float*>(w < 2 ? &zsA[0] : &zsB[0]) + (w & 1) * (16 * EP);
-    const int co_w = ct * CO_TILE_F32 + 64 * w;
+    // two 16 x (128+4) float tiles (16.9 KB) fit in each 18.4 KB staging buffer and in
+    // each raw array
+    uint16_t* eb = w < 2 ? &zsA[0] : w < 4 ? &zsB[0] : w < 6 ? &raw0[0] : &raw1[0];
+    float* ep = reinterpret_cast<float*>(eb) + (w & 1) * (16 * EP);
+    const int co_w = ct * CO_T + 64 * w;
     // after the transpose, lane (lq, l16) holds rows lq + 4i (i = 0..3) of each block,
     // time steps t0 + 8*l16 .. +7
     float bia[4][4];
@@ -521,18 +535,38 @@ hipError_t launch_prep_bf16(const float* W, int C_out, int C_in, int Cout_pad, i
   return hipGetLastError();
 }
 
-hipError_t launch_conv_bf16(const ConvF32Args& a, hipStream_t stream) {
+int conv_bf16_co_tile(long long N, int L_out, int C_out) {
+  // The 512-channel tile when it pads C_out no further than the 256-channel one and its
+  // grid still fills every CU at least once (one 8-wave workgroup per CU).
+  const long long tiles512 = (C_out + 511) / 512;
+  const long long wgs = N * ((L_out + TTB - 1) / TTB) * tiles512;
+  return (round_up(C_out, 512) == round_up(C_out, 256) && wgs >= 256) ? 512 : 256;
+}
+
+hipError_t launch_conv_bf16(const ConvF32Args& a, int co_tile, hipStream_t stream) {
   const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // the repacked weights and the folded scale/shift must cover every channel the grid's
+  // tiles touch
+  if ((co_tile != 256 && co_tile != 512) || a.NCB * 16 < a.n_ct * co_tile)
+    return hipErrorInvalidValue;
   // every tap offset and tile start is even, L is even and x is 4-byte aligned: each
   // lane can load an aligned pair of time steps
   const bool pair = ((a.dil | a.pad | a.L_in) & 1) == 0 &&
                     (reinterpret_cast<uintptr_t>(a.x) & 3) == 0;
-  if (pair)
-    hipLaunchKernelGGL(conv_bf16_kernel<true>, dim3((unsigned)nwg), dim3(NTHREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(conv_bf16_kernel<false>, dim3((unsigned)nwg), dim3(NTHREADS), 0, stream, a);
+  const dim3 grid((unsigned)nwg);
+  if (co_tile == 512) {
+    if (pair)
+      hipLaunchKernelGGL((conv_bf16_kernel<true, 8>), grid, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((conv_bf16_kernel<false, 8>), grid, dim3(512), 0, stream, a);
+  } else {
+    if (pair)
+      hipLaunchKernelGGL((conv_bf16_kernel<true, 4>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((conv_bf16_kernel<false, 4>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -44,8 +44,8 @@ hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, in
                            float* shift, hipStream_t stream);
 
 // conv_f32.hip
-// Tile shape of the float32 kernel: tt time steps, 16*mb output channels per wave,
-// 4 waves, so 64*mb output channels per workgroup.
+// Tile shape: tt time steps and 64*mb output channels per workgroup (float32 kernel:
+// 4 waves of 16*mb channels; bf16 kernel: mb waves of 64 channels).
 struct ConvTile {
   int tt, mb;
   int co_tile() const { return 64 * mb; }
@@ -62,7 +62,10 @@ hipError_t launch_prep_bf16(const float* W, int C_out, int C_in, int Cout_pad, i
                             void* Wp, const float* running_mean, const float* running_var,
                             const float* gamma, const float* beta, float eps, float* scale,
                             float* shift, hipStream_t stream);
-hipError_t launch_conv_bf16(const ConvF32Args& a, hipStream_t stream);
+// Output channels per bf16 workgroup (256: 4 waves, or 512: 8 waves) for this shape;
+// Cout_pad and n_ct follow from it, and launch_conv_bf16 takes the same value.
+int conv_bf16_co_tile(long long N, int L_out, int C_out);
+hipError_t launch_conv_bf16(const ConvF32Args& a, int co_tile, hipStream_t stream);
 
 // bn_train.hip: training-mode BN statistics. Time steps of one (n, c) row per
 // statistics workgroup; the partials hold one (sum, sum of squares) double pair per

@@ -62,7 +62,9 @@ def test_external_bn_f32_matches_oracle(N, C, L, d):
     assert err <= TOL_F32, err
 
 
-@pytest.mark.parametrize("N,C,L,d", [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128)])
+# (4, 512, 8190, 7) runs the 512-channel (8-wave) bf16 tile
+@pytest.mark.parametrize("N,C,L,d", [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128),
+                                     (4, 512, 8190, 7)])
 def test_external_bn_bf16_matches_oracle(N, C, L, d):
     seed = 60_000 + N + C + L + d
     announce("relu_dconv1d_residual_fwd_bf16", (N, C, L, d), "seed", seed)

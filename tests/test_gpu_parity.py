@@ -114,8 +114,14 @@ def test_block_f32_matches_oracle(N, C, L, d):
     assert err <= TOL_F32, err
 
 
-@pytest.mark.parametrize("N,C,L,d", [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128),
-                                     (2, 300, 300, 300), (2, 16, 512, 128)])
+# The last two run the 512-channel (8-wave) bf16 tile, which wide layers get when the grid
+# still has a workgroup per CU: C=384 padded to 512 on the paired-load path, and C=512
+# with an odd dilation on the 2-byte-load path.
+BF16_CASES = [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128), (2, 300, 300, 300),
+              (2, 16, 512, 128), (2, 384, 16384, 128), (4, 512, 8190, 7)]
+
+
+@pytest.mark.parametrize("N,C,L,d", BF16_CASES)
 def test_block_bf16_matches_oracle(N, C, L, d):
     seed = 20_000 + N + C + L + d
     announce("prenorm_dconv1d_fwd_bf16", (N, C, L, d), "seed", seed)

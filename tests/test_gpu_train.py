@@ -80,8 +80,9 @@ def test_train_f32_matches_oracle(N, C, L, d):
     check(run_train(p, d, 0.1), oracle_train(p, d, 0.1), p["eps"], TOL_F32)
 
 
+# (2, 384, 16384, 128) runs the 512-channel (8-wave) bf16 tile
 @pytest.mark.parametrize("N,C,L,d", [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128),
-                                     (2, 16, 512, 128)])
+                                     (2, 16, 512, 128), (2, 384, 16384, 128)])
 def test_train_bf16_matches_oracle(N, C, L, d):
     seed = 40_000 + N + C + L + d
     announce("prenorm_dconv1d_fwd_train_bf16", (N, C, L, d), "seed", seed)
