@@ -114,11 +114,13 @@ def test_block_f32_matches_oracle(N, C, L, d):
     assert err <= TOL_F32, err
 
 
-# The last two run the 512-channel (8-wave) bf16 tile, which wide layers get when the grid
-# still has a workgroup per CU: C=384 padded to 512 on the paired-load path, and C=512
-# with an odd dilation on the 2-byte-load path.
+# The last five run the 512-channel (8-wave) bf16 tile, which wide layers get when the
+# grid still has a workgroup per CU: C=384 padded to 512 on the paired-load path; C=512
+# with an odd dilation on the 2-byte-load path; C=300 with a 2-step ragged last tile
+# (per-element epilogue); C=320 with L a multiple of 8 (16-byte epilogue); and an odd L.
 BF16_CASES = [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128), (2, 300, 300, 300),
-              (2, 16, 512, 128), (2, 384, 16384, 128), (4, 512, 8190, 7)]
+              (2, 16, 512, 128), (2, 384, 16384, 128), (4, 512, 8190, 7),
+              (1, 300, 32770, 2), (1, 320, 32768, 130), (2, 288, 16383, 5)]
 
 
 @pytest.mark.parametrize("N,C,L,d", BF16_CASES)
