@@ -28,6 +28,13 @@
 //                loads) two chunks ahead of their use, so x latency has two chunks to
 //                hide in and no staging registers are held across the MFMAs; otherwise
 //                two 2-byte loads into registers, one chunk ahead.
+//   schedule   = (paired path) a chunk's buffer->LDS loads are issued one row per
+//                16-column block among the first K-step's MFMAs rather than in one burst
+//                after the barrier, B operands run three blocks ahead through a 4-deep
+//                register ring, and with 8 waves the waves sharing a SIMD (w and w+4)
+//                run in opposite order: waves 0-3 do their MFMAs and then stage the next
+//                chunk, waves 4-7 stage first, so each SIMD has MFMAs to run while one of
+//                its waves stages.
 //
 // K-slot mapping: in K-step s of a chunk, quarter-wave q = lane/16 element e (0..7) is
 // chunk row 32s + 8q + e, for A and B alike, so the sum over K is the plain sum over
@@ -179,26 +186,26 @@ conv_bf16_kernel(ConvF32Args a) {
     }
     load_bn(q);
   };
-  // Paired path: chunk q's raw x rows of this wave, one row of 128 steps per load (64
-  // lanes x 4 bytes), straight into LDS.
-  auto dma_x0 = [&](int q) {
+  // Paired path: rows [i0, i0 + cnt) of chunk q's raw x rows of this wave, one row of 128
+  // steps per load (64 lanes x 4 bytes), straight into LDS.
+  auto dma_x0 = [&](int q, int i0 = 0, int cnt = KCB / WV) {
     const int c = q / 3, k = q - 3 * c;
     const int ts = t0 + 2 * l + k * a.dil - a.pad;
     const int vo = 2 * min(max(ts, 0), a.L_in - 2);
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
+    for (int i = i0; i < i0 + cnt; ++i) {
       const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void*)&raw0[(RPW * w + i) * TTB], 4, vo,
           row_bytes(ci), 0, 0);
     }
   };
-  auto dma_x1 = [&](int q) {
+  auto dma_x1 = [&](int q, int i0 = 0, int cnt = KCB / WV) {
     const int c = q / 3, k = q - 3 * c;
     const int ts = t0 + 2 * l + k * a.dil - a.pad;
     const int vo = 2 * min(max(ts, 0), a.L_in - 2);
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
+    for (int i = i0; i < i0 + cnt; ++i) {
       const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void*)&raw1[(RPW * w + i) * TTB], 4, vo,
@@ -284,28 +291,59 @@ conv_bf16_kernel(ConvF32Args a) {
 
   // One chunk (two K-steps) on LDS buffer zb. `next` stages the next chunk into the
   // other buffer after the chunk's MFMAs, the latest point before the barrier, which
-  // gives its x loads the longest time to arrive.
-  auto compute = [&](const uint16_t* zb, int q, auto P, auto&& next) {
+  // gives its x loads the longest time to arrive; on the paired path with 8 waves,
+  // waves 4-7 (`early`) stage before their MFMAs instead. `dma(nb)` issues this wave's
+  // buffer->LDS rows of a later chunk among the MFMAs of the first K-step's block nb
+  // (paired path; the other path loads x into registers before the chunk).
+  const bool early = PAIR && WV == 8 && w >= 4;
+  auto compute = [&](const uint16_t* zb, int q, auto P, auto&& next, auto&& dma) {
     constexpr int par = decltype(P)::value;
+    if constexpr (PAIR) {
+      if (early) next();
+      constexpr int BR = 4, BP = 3;
+      bf16x8 bv[BR];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int S = 2 * q + s;
-      load_w(S + DIST, wr[(2 * par + s + DIST) % RING]);
-      bf16x8 bv[2];
-      bv[0] = load_b(zb, s, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < BP; ++i) bv[i] = load_b(zb, i / NB, i % NB);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if (nb + 1 < NB) bv[(nb + 1) & 1] = load_b(zb, s, nb + 1);
+      for (int s = 0; s < 2; ++s) {
+        const int S = 2 * q + s;
+        load_w(S + DIST, wr[(2 * par + s + DIST) % RING]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, wr[(2 * par + s) % RING][mb]), bv[nb & 1],
-              acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          const int it = s * NB + nb;
+          if (s == 0) dma(nb);
+          if (it + BP < 2 * NB) bv[(it + BP) % BR] = load_b(zb, (it + BP) / NB, (it + BP) % NB);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, wr[(2 * par + s) % RING][mb]), bv[it % BR],
+                acc[mb][nb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (!early) next();
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int S = 2 * q + s;
+        load_w(S + DIST, wr[(2 * par + s + DIST) % RING]);
+        bf16x8 bv[2];
+        bv[0] = load_b(zb, s, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          if (nb + 1 < NB) bv[(nb + 1) & 1] = load_b(zb, s, nb + 1);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, wr[(2 * par + s) % RING][mb]), bv[nb & 1],
+                acc[mb][nb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      next();
     }
-    next();
   };
 
   // Two chunks per trip. The staged chunk index is clamped to the last chunk, so the
@@ -315,9 +353,9 @@ conv_bf16_kernel(ConvF32Args a) {
 #pragma unroll
   for (int S = 0; S < DIST; ++S) load_w(S, wr[S]);
   if constexpr (PAIR) {
-    // Chunk q: start the buffer->LDS loads of chunk q+2 (into the raw array chunk q was
-    // staged from), run chunk q's MFMAs, then stage chunk q+1 from the other raw array
-    // (loaded during chunk q-1). The barrier carries no memory fence: the release fence
+    // Chunk q: run chunk q's MFMAs, issuing among them the buffer->LDS loads of chunk q+2
+    // (into the raw array chunk q was staged from), and stage chunk q+1 from the other
+    // raw array (loaded during chunk q-1). The barrier carries no memory fence: the release fence
     // of __syncthreads would wait for the chunk q+2 loads still in flight. Nothing needs
     // it: raw rows are read only by the wave that loaded them (the compiler waits for its
     // own loads before the read), and the staged z writes are complete once lgkmcnt is 0.
@@ -329,23 +367,22 @@ conv_bf16_kernel(ConvF32Args a) {
     read_raw0();
     store_z(0, zsA);
     bar();
+    constexpr int RPI = RPW / NB;   // raw rows loaded per 16-column block of K-step 0
     for (int q = 0; q < Q; q += 2) {
-      dma_x0(min(q + 2, Q - 1));
       load_bn(q + 1);
       __builtin_amdgcn_sched_barrier(0);
       compute(zsA, q, Parity<0>{}, [&] {
         read_raw1();
         store_z(q + 1, zsB);
-      });
+      }, [&](int it) { dma_x0(min(q + 2, Q - 1), it * RPI, RPI); });
       bar();
       const int qn = min(q + 2, Q - 1);
-      dma_x1(min(q + 3, Q - 1));
       load_bn(qn);
       __builtin_amdgcn_sched_barrier(0);
       compute(zsB, q + 1, Parity<1>{}, [&] {
         read_raw0();
         store_z(qn, zsA);
-      });
+      }, [&](int it) { dma_x1(min(q + 3, Q - 1), it * RPI, RPI); });
       bar();
     }
   } else {
@@ -355,12 +392,12 @@ conv_bf16_kernel(ConvF32Args a) {
     for (int q = 0; q < Q; q += 2) {
       load_x(q + 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(zsA, q, Parity<0>{}, [&] { store_z(q + 1, zsB); });
+      compute(zsA, q, Parity<0>{}, [&] { store_z(q + 1, zsB); }, [](int) {});
       __syncthreads();
       const int qn = min(q + 2, Q - 1);
       load_x(qn);
       __builtin_amdgcn_sched_barrier(0);
-      compute(zsB, q + 1, Parity<1>{}, [&] { store_z(qn, zsA); });
+      compute(zsB, q + 1, Parity<1>{}, [&] { store_z(qn, zsA); }, [](int) {});
       __syncthreads();
     }
   }
