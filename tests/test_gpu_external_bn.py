@@ -62,9 +62,10 @@ def test_external_bn_f32_matches_oracle(N, C, L, d):
     assert err <= TOL_F32, err
 
 
-# (4, 512, 8190, 7) runs the 512-channel (8-wave) bf16 tile
+# (4, 512, 8190, 7) and (2, 384, 16384, 64) run the 512-channel (8-wave) bf16 tile, on the
+# 2-byte-load and the paired-load path
 @pytest.mark.parametrize("N,C,L,d", [(1, 3, 7, 2), (2, 96, 777, 50), (8, 64, 8200, 128),
-                                     (4, 512, 8190, 7)])
+                                     (4, 512, 8190, 7), (2, 384, 16384, 64)])
 def test_external_bn_bf16_matches_oracle(N, C, L, d):
     seed = 60_000 + N + C + L + d
     announce("relu_dconv1d_residual_fwd_bf16", (N, C, L, d), "seed", seed)
@@ -73,10 +74,11 @@ def test_external_bn_bf16_matches_oracle(N, C, L, d):
     assert err <= TOL_BF16, err
 
 
-@pytest.mark.parametrize("bf16", [False, True])
-def test_external_bn_inplace_residual(bf16):
-    """out = residual (the same buffer) gives the out-of-place result."""
-    N, C, L, d = 4, 80, 3000, 40
+@pytest.mark.parametrize("bf16,N,C,L,d", [(False, 4, 80, 3000, 40), (True, 4, 80, 3000, 40),
+                                          (True, 2, 384, 16384, 64)])
+def test_external_bn_inplace_residual(bf16, N, C, L, d):
+    """out = residual (the same buffer) gives the out-of-place result (the last case runs
+    the 8-wave bf16 tile)."""
     announce("relu_dconv1d_residual in place", (N, C, L, d), "bf16", bf16)
     p = ext_inputs(N, C, L, 50_900 + bf16, bf16=bf16)
     ref = run_ext(p, d, bf16=bf16)

@@ -16,6 +16,15 @@ pytestmark = pytest.mark.gpu
 RNG = np.random.default_rng(20260101)
 BLOCK_SHAPES = [(int(RNG.integers(1, 5)), int(RNG.integers(1, 150)), int(RNG.integers(1, 700)),
                  int(RNG.integers(1, 800))) for _ in range(24)]
+# wide layers that take the 512-channel (8-wave) bf16 tile: 256 < C <= 512 and at least one
+# workgroup per CU (N * ceil(L / 128) >= 256)
+RNG_WIDE = np.random.default_rng(20261202)
+WIDE_BF16_SHAPES = []
+for _ in range(4):
+    n_ = int(RNG_WIDE.integers(1, 3))
+    WIDE_BF16_SHAPES.append((n_, int(RNG_WIDE.integers(257, 513)),
+                             256 * 128 // n_ + int(RNG_WIDE.integers(0, 3000)),
+                             int(RNG_WIDE.integers(1, 3000))))
 GN_SHAPES = []
 for _ in range(12):
     G = int(RNG.choice([1, 2, 3, 4, 8]))
@@ -52,6 +61,21 @@ def test_random_block(N, C, L, d, mode):
     torch.cuda.synchronize()
     err = maxrel(out.float().cpu().numpy(), ref)
     assert err <= (TOL_BF16 if bf16 else TOL_F32), err
+
+
+@pytest.mark.parametrize("N,C,L,d", WIDE_BF16_SHAPES)
+def test_random_wide_bf16_block(N, C, L, d):
+    seed = 97_000 + N * 1000 + C * 7 + L + d
+    announce("random wide bf16 block", (N, C, L, d), "seed", seed)
+    p = prenorm_inputs(N, C, L, seed, bf16=True)
+    q = to_dev(p)
+    out = dc.prenorm_dconv1d_fwd_bf16(q["x"], q["running_mean"], q["running_var"], q["gamma"],
+                                      q["beta"], q["eps"], q["W"], q["b"], d)
+    torch.cuda.synchronize()
+    ref = oracle.prenorm_block(p["x"], p["running_mean"], p["running_var"], p["gamma"],
+                               p["beta"], p["eps"], p["W"], p["b"], d)
+    err = maxrel(out.float().cpu().numpy(), ref)
+    assert err <= TOL_BF16, err
 
 
 @pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil,bias", GN_SHAPES)
