@@ -28,20 +28,29 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv_f32_prenorm_N32_C256_L4096_d128.json")
+# committed PMC traffic records of the dominant kernel, per block workload (eval-mode BN)
+TRAFFIC_FILES = {
+    1: ("conv_f32_kernel", os.path.join(ROOT, "profiles",
+                                        "traffic_conv_f32_prenorm_N32_C256_L4096_d128.json")),
+    4: ("conv_bf16_kernel", os.path.join(ROOT, "profiles",
+                                         "traffic_conv_bf16_prenorm_N16_C512_L16384_d128.json")),
+}
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed PMC summary, or
     None when there is none or the kernel source changed since it was taken."""
+    if workload not in TRAFFIC_FILES:
+        return None
+    kernel, path = TRAFFIC_FILES[workload]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     from normalisation_dilated_conv1d_amd.profiling import source_digest
 
-    if t.get("source_sha256") != source_digest("conv_f32_kernel"):
+    if t.get("kernel") != kernel or t.get("source_sha256") != source_digest(kernel):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -269,8 +278,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(k_tflops, 3),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(k_tflops / peak, 4),
-                     "traffic": (measured_traffic()
-                                 if args.workload == 1 and args.bn == "eval" else None),
+                     "traffic": (measured_traffic(args.workload)
+                                 if args.bn == "eval" else None),
                      "kernel": kernel_name,
                      "kernel_ms": round(kern_ms_avg, 5),
                      "algorithmic_flops_per_launch": flops,
