@@ -188,12 +188,13 @@ def main():
                                     G, w["padding"], w["dilation"], out=out)
 
         flops = 2.0 * N * T_out * C_out * 3 * C_in
-        # x once, y written and read back, out written, W and the affine vectors
-        alg_bytes = 4.0 * (N * C_in * T + 3 * N * C_out * T_out + 3 * C_in * C_out + 2 * C_out)
+        # one launch (every group inside one workgroup): x once, out written once, W and
+        # the affine vectors; the conv output never reaches HBM
+        alg_bytes = 4.0 * (N * C_in * T + N * C_out * T_out + 3 * C_in * C_out + 2 * C_out)
         config = {"workload": wl.name, "N": N, "C_in": C_in, "C_out": C_out, "T": T,
                   "num_groups": G, "kernel_size": 3, "padding": w["padding"],
                   "dilation": w["dilation"], "parallelism": "single GPU"}
-        kernel_name = "conv_f32_kernel<64, no BN, GroupNorm statistics, float>"
+        kernel_name = "conv_gn_fused_kernel<17>"
 
     for _ in range(args.warmup):
         step()

@@ -201,10 +201,15 @@ int relu_dconv1d_residual_fwd_bf16(const uint16_t* xn, const float* W, const flo
  *                must not overlap x
  *   padding >= 0, dilation >= 1; T_out must be >= 1
  *
- * The conv stores its result into out while writing per-(sample, channel, time tile)
- * partial sums and centred sums of squares to the workspace; a second kernel merges
- * them per (sample, group) in a fixed order in double precision and normalises out in
- * place. Results are bitwise reproducible from run to run.
+ * When every group lies inside 16 output channels (C_out/num_groups divides 16),
+ * C_in and C_out are multiples of 16, T_out <= 1024, W is 8-byte aligned and the input
+ * window 128*ceil(T_out/128) + 2*dilation is at most 1216 steps, one kernel does it all:
+ * the conv result stays on chip, the group statistics are reduced per (sample, group)
+ * in a fixed order and out is written once; no workspace is used. Otherwise the conv
+ * stores its result into out while writing per-(sample, channel, time tile) partial
+ * sums and centred sums of squares to the workspace, and a second kernel merges them
+ * per (sample, group) in a fixed order in double precision and normalises out in
+ * place. Either way results are bitwise reproducible from run to run.
  */
 int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias,
                          const float* gamma, const float* beta, float eps,

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "dconv1d.h"
+#include "conv_gn.h"
 #include "internal.h"
 
 using namespace dconv1d;
@@ -377,6 +378,34 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
   const int n_tt = (Lo + tile.tt - 1) / tile.tt;
   if (N * n_tt * n_ct > kMaxIndex) return fail(DCONV1D_EINVAL, "grid too large");
   if (N == 0) return DCONV1D_OK;
+
+  // Every group inside 16 output channels and T_out <= 1024: one launch, no workspace.
+  const int cpg = (int)(C_out / num_groups);
+  if (gn_fused_fits(N, (int)C_in, (int)C_out, Lo, (int)dilation, cpg, W)) {
+    GnFusedArgs g{};
+    g.x = x;
+    g.W = W;
+    g.bias = bias;
+    g.gamma = gamma;
+    g.beta = beta;
+    g.out = out;
+    g.eps = eps;
+    g.N = (int)N;
+    g.C_in = (int)C_in;
+    g.C_out = (int)C_out;
+    g.T = (int)T;
+    g.T_out = Lo;
+    g.pad = (int)padding;
+    g.dil = (int)dilation;
+    g.cpg = cpg;
+    g.mg = gn_fused_groups(Lo, (int)dilation);
+    g.n_cb = (int)C_out / 16;
+    const int slot = timer_begin(stream);
+    hipError_t e = launch_conv_gn_fused(g, stream);
+    timer_end(slot, stream);
+    if (e != hipSuccess) return hip_fail(e, "conv+groupnorm kernel launch");
+    return DCONV1D_OK;
+  }
 
   const size_t off_wp = 0;
   const size_t off_part = align256(off_wp + sizeof(float) * 3 * (size_t)Cin_pad * Cout_pad);

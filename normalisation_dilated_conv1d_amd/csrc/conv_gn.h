@@ -1,0 +1,31 @@
+// Declarations of the single-launch Conv1d + GroupNorm kernel (conv_gn.hip), shared with
+// the C ABI (api.hip). Not part of the ABI.
+#pragma once
+
+#include "internal.h"
+
+namespace dconv1d {
+
+// conv_gn.hip: Conv1d + GroupNorm in one launch when every group fits in a workgroup of
+// 16 output channels x T_out <= 1024 steps. The staged window is 64*mg steps wide
+// (gn_fused_groups; 0 when no instantiated width covers the shape).
+constexpr int GN_MG_MAX = 19;
+struct GnFusedArgs {
+  const float* x;       // [N][C_in][T]
+  const float* W;       // [C_out][C_in][3], 8-byte aligned
+  const float* bias;    // [C_out] or nullptr
+  const float* gamma;   // [C_out] or nullptr (1)
+  const float* beta;    // [C_out] or nullptr (0)
+  float* out;           // [N][C_out][T_out]
+  float eps;
+  int N, C_in, C_out, T, T_out;
+  int pad, dil;         // tap k reads input t - pad + k*dil
+  int cpg;              // channels per group (divides 16)
+  int mg;               // staged window width in 64-step groups, gn_fused_groups(T_out, dil)
+  int n_cb;             // C_out / 16
+};
+int gn_fused_groups(int T_out, int dil);
+bool gn_fused_fits(long long N, int C_in, int C_out, int T_out, int dil, int cpg, const void* W);
+hipError_t launch_conv_gn_fused(const GnFusedArgs& a, hipStream_t stream);
+
+}  // namespace dconv1d

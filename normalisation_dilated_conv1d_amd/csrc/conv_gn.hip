@@ -1,0 +1,327 @@
+// Conv1d + GroupNorm in one launch, for shapes whose groups fit in one workgroup
+// (POPCORNBENCH "FW-GLM-5-1__l2_p35", its single turn: the conv with zero padding, then
+// per (sample, group) the mean and the biased variance over the group's channels and
+// time steps, normalisation with eps inside the square root, optional affine).
+//
+// Work split
+//   workgroup  = one sample n and 16 output channels [co0, co0 + 16) over every output
+//                time step (T_out <= 1024). Channels per group divides 16, so every group
+//                lies inside one workgroup: the conv result stays in registers, the group
+//                statistics are reduced inside the workgroup in a fixed order, and `out`
+//                is written once, already normalised. No second pass over HBM, no weight
+//                repack launch.
+//   waves      = 8; wave w owns output steps [128w, 128w + 128): 8 accumulator blocks of
+//                16 x 16 (v_mfma_f32_16x16x4_f32, float32 products and accumulation).
+//   K loop     = chunks of 16 input channels. A chunk stages x[n][16c .. 16c + 16) over the
+//                window of input steps [-pad, -pad + 64*MG) that every tap of every
+//                output step reads, once, into LDS: tap k of output step t reads window
+//                column t + k*dil, so the three taps share one staged copy and x crosses
+//                L2 -> LDS once per workgroup. Wave w stages channels 16c + w and
+//                16c + w + 8: MG buffer loads of 64 steps per channel into registers, two
+//                chunks ahead (chunk c + 2 loads
+//                while chunk c computes; chunk c + 1, loaded during chunk c - 1, goes to
+//                LDS after chunk c's MFMAs), then one 256-byte ds_write per load. Steps
+//                outside [0, T) get an offset past the end of the row's buffer range, so
+//                the hardware range check delivers exact zeros. Two LDS buffers, one
+//                barrier per chunk. (Loads straight into LDS were tried: the compiler
+//                then waits for every one of them before each LDS read.)
+//   LDS layout = row r (channel 16c + r) at r*RS floats, RS = 64*MG + 8: RS = 8 mod 16
+//                puts the rows 2lq of the four quarter-waves of a B read on different
+//                banks.
+//   operands   = MFMA K-step (tap k, half g, e): quarter-wave lq = lane/16 supplies input
+//                channel 16c + 8g + 2lq + e. A = W[co0 + lane%16][16c + 8g + 2lq + e][k]:
+//                per half, six consecutive floats of the [C_out][C_in][3] layout per lane.
+//                B = window column t + k*dil of row 8g + 2lq + e. 96 MFMAs per wave per
+//                chunk between barriers.
+//   statistics = two passes over the registers: per-row sums (quarter-wave butterflies),
+//                then per group, in double, over (wave, row) in a fixed order -> mean;
+//                the same for the sum of squared deviations from that mean -> biased
+//                variance. Bitwise reproducible: no atomics, no order that depends on
+//                timing.
+
+#include "conv_gn.h"
+
+namespace dconv1d {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int GN_WAVES = 8;
+constexpr int GN_CI = 16;     // input channels per chunk
+constexpr int GN_NB = 8;      // 16-column blocks per wave
+// buffer resource word 3 for raw (untyped, unswizzled) buffers on gfx9-family parts
+constexpr int kBufferFlags = 0x00020000;
+// voffset that fails the range check of any row (rows are < 2^31 bytes)
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <int XOR>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (XOR << 10) | 0x1F));
+}
+// sum over the 16 lanes of each quarter-wave; every lane ends with the same value
+__device__ __forceinline__ float quarterwave_sum(float v) {
+  v += swz_xor<8>(v);
+  v += swz_xor<4>(v);
+  v += swz_xor<2>(v);
+  v += swz_xor<1>(v);
+  return v;
+}
+
+}  // namespace
+
+// MG: 64-step groups of the staged window (the window is 64*MG steps wide)
+template <int MG>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * GN_WAVES, 64 * GN_WAVES)))
+conv_gn_fused_kernel(GnFusedArgs a) {
+  constexpr int RS = 64 * MG + 8;             // floats per staged row
+  constexpr int BUF = GN_CI * RS;             // floats per chunk buffer
+  __shared__ __attribute__((aligned(16))) float zA[BUF];
+  __shared__ __attribute__((aligned(16))) float zB[BUF];
+  __shared__ float red[GN_WAVES * 16];   // per (wave, row) partial of the current pass
+  __shared__ float gmean[16], grstd[16];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int lq = l >> 4;
+  const int l16 = l & 15;
+
+  // XCD-aware order: workgroup b runs on XCD b % 8; consecutive logical indices (the
+  // channel blocks of one sample, which read the same x) land on one XCD and its L2
+  const int nwg = gridDim.x;
+  const int b = blockIdx.x;
+  const int per = nwg >> 3, rem = nwg & 7, xcd = b & 7;
+  const int logical = xcd * per + min(xcd, rem) + (b >> 3);
+  const int cb = __builtin_amdgcn_readfirstlane(logical % a.n_cb);
+  const int n = __builtin_amdgcn_readfirstlane(logical / a.n_cb);
+  const int co0 = 16 * cb;
+  const int tw = 128 * w;                 // first output step of this wave
+  const bool active = tw < a.T_out;       // waves past the end only stage
+
+  const float* xn = a.x + (size_t)n * a.C_in * a.T;
+  // lane's A operands of chunk c: W[co0 + l16][8c + 2lq + e][k] at wrow + 24c + 3e + k
+  const float* __restrict__ wrow = a.W + ((size_t)(co0 + l16) * a.C_in + 2 * lq) * 3;
+
+  f32x4 acc[GN_NB];
+#pragma unroll
+  for (int nb = 0; nb < GN_NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[nb][r] = 0.f;
+
+  // byte offset of window step 64m + l in its row: input step t = 64m + l - pad, or an
+  // offset the range check rejects (t < 0; t >= T is past the range by itself). Opaque,
+  // so that no constant part is folded into the instruction offset (which could bring a
+  // rejected offset back into range).
+  uint32_t voff[MG];
+#pragma unroll
+  for (int m = 0; m < MG; ++m) {
+    const int t = 64 * m + l - a.pad;
+    voff[m] = t >= 0 ? 4u * (uint32_t)t : kOutOfRange;
+    asm volatile("" : "+v"(voff[m]));
+  }
+  // this wave's rows of chunk c (channels 16c + w and 16c + w + 8): MG loads of 64
+  // steps each into registers
+  float xa[2][MG], xb[2][MG];
+  auto load_x = [&](int c, float (&dst)[2][MG]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(xn + (size_t)(GN_CI * c + w + 8 * h) * a.T), (short)0, 4 * a.T,
+          kBufferFlags);
+#pragma unroll
+      for (int m = 0; m < MG; ++m)
+        dst[h][m] =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff[m], 0, 0));
+    }
+  };
+  auto store_x = [&](const float (&src)[2][MG], float* zb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < MG; ++m) zb[(w + 8 * h) * RS + 64 * m + l] = src[h][m];
+  };
+  const int nC = a.C_in / GN_CI;
+  // A operands of chunk c: W[co0 + l16][16c + 8g + 2lq + e][k] at wrow + 48c + 24g + 3e + k,
+  // stored at index 6g + 3e + k
+  auto load_w = [&](int c, float (&dst)[12]) {
+    c = min(c, nC - 1);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const f32x2* p = reinterpret_cast<const f32x2*>(wrow + 48 * c + 24 * g);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const f32x2 v = p[i];
+        dst[6 * g + 2 * i] = v[0];
+        dst[6 * g + 2 * i + 1] = v[1];
+      }
+    }
+  };
+  // B operand base of this lane: row 2lq, window column tw + l16
+  const int boff = 2 * lq * RS + tw + l16;
+  // the chunk's 96 MFMAs of this wave on buffer zb, in six steps (tap k, half g); the B
+  // operands of the next step are read while the current step's MFMAs run
+  auto compute = [&](const float* zb, const float (&wv)[12]) {
+    if (!active) return;
+    const float* base = zb + boff;
+    auto read_b = [&](int st, f32x2 (&dst)[GN_NB]) {
+      const float* p = base + 8 * (st & 1) * RS + (st >> 1) * a.dil;
+#pragma unroll
+      for (int nb = 0; nb < GN_NB; ++nb) {
+        dst[nb][0] = p[16 * nb];
+        dst[nb][1] = p[16 * nb + RS];
+      }
+    };
+    f32x2 bv[2][GN_NB];
+    read_b(0, bv[0]);
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
+      if (st + 1 < 6) read_b(st + 1, bv[(st + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int k = st >> 1, g = st & 1;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int nb = 0; nb < GN_NB; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[6 * g + 3 * e + k], bv[st & 1][nb][e],
+                                                         acc[nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // one chunk: the weights of chunk c + 1 and the x row of chunk c + 2 go out, chunk c
+  // computes from buffer zc, then chunk c + 1's row (loaded a chunk ago) goes to buffer zn
+  // (last read by chunk c - 1, which every wave finished before the previous barrier)
+  auto chunk = [&](int c, const float* zc, float* zn, const float (&wc)[12], float (&w1)[12],
+                   float (&x2)[2][MG], const float (&x1)[2][MG]) {
+    load_w(c + 1, w1);
+    load_x(min(c + 2, nC - 1), x2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(zc, wc);
+    if (c + 1 < nC) store_x(x1, zn);
+    __syncthreads();
+  };
+
+  float wA[12], wB[12];
+  load_w(0, wA);
+  load_x(0, xa);
+  load_x(min(1, nC - 1), xb);
+  store_x(xa, zA);
+  __syncthreads();
+  int c = 0;
+  for (; c + 1 < nC; c += 2) {
+    chunk(c, zA, zB, wA, wB, xa, xb);
+    chunk(c + 1, zB, zA, wB, wA, xb, xa);
+  }
+  if (c < nC) chunk(c, zA, zB, wA, wB, xa, xb);
+
+  // Epilogue. Register r of block nb holds channel co0 + 4lq + r, step tw + 16nb + l16.
+  const int cpg = a.cpg;
+  const int ngr = 16 / cpg;   // groups in this workgroup
+  const double cnt = (double)cpg * (double)a.T_out;
+  float y[GN_NB][4];
+  bool valid[GN_NB];
+#pragma unroll
+  for (int nb = 0; nb < GN_NB; ++nb) valid[nb] = tw + 16 * nb + l16 < a.T_out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float bco = a.bias ? a.bias[co0 + 4 * lq + r] : 0.f;
+#pragma unroll
+    for (int nb = 0; nb < GN_NB; ++nb) y[nb][r] = acc[nb][r] + bco;
+  }
+
+  // pass 1: the group means
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float s = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < GN_NB; ++nb) s += valid[nb] ? y[nb][r] : 0.f;
+    s = quarterwave_sum(s);
+    if (l16 == 0) red[w * 16 + 4 * lq + r] = s;
+  }
+  __syncthreads();
+  if (tid < ngr) {
+    double tot = 0.0;
+    for (int ww = 0; ww < GN_WAVES; ++ww)
+      for (int i = 0; i < cpg; ++i) tot += (double)red[ww * 16 + tid * cpg + i];
+    gmean[tid] = (float)(tot / cnt);
+  }
+  __syncthreads();
+
+  // pass 2: the biased variances, from the deviations about those means
+  float mean[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) mean[r] = gmean[(4 * lq + r) / cpg];
+  // (the barrier above also ends the pass-1 reads of red, so red can be rewritten)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float s = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < GN_NB; ++nb) {
+      const float dv = y[nb][r] - mean[r];
+      s += valid[nb] ? dv * dv : 0.f;
+    }
+    s = quarterwave_sum(s);
+    if (l16 == 0) red[w * 16 + 4 * lq + r] = s;
+  }
+  __syncthreads();
+  if (tid < ngr) {
+    double tot = 0.0;
+    for (int ww = 0; ww < GN_WAVES; ++ww)
+      for (int i = 0; i < cpg; ++i) tot += (double)red[ww * 16 + tid * cpg + i];
+    grstd[tid] = (float)(1.0 / sqrt(tot / cnt + (double)a.eps));
+  }
+  __syncthreads();
+
+  // normalise and store: out = (y - mean) * rstd * gamma + beta
+  float* __restrict__ outn = a.out + (size_t)n * a.C_out * a.T_out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int co = co0 + 4 * lq + r;
+    const float ga = a.gamma ? a.gamma[co] : 1.f;
+    const float be = a.beta ? a.beta[co] : 0.f;
+    const float sc = grstd[(4 * lq + r) / cpg] * ga;
+    float* __restrict__ orow = outn + (size_t)co * a.T_out;
+#pragma unroll
+    for (int nb = 0; nb < GN_NB; ++nb) {
+      const int t = tw + 16 * nb + l16;
+      if (valid[nb]) orow[t] = fmaf(y[nb][r] - mean[r], sc, be);
+    }
+  }
+}
+
+int gn_fused_groups(int T_out, int dil) {
+  const long long span = 128LL * ((T_out + 127) / 128) + 2LL * dil;
+  const int need = (int)((span + 63) / 64);
+  for (int mg : {4, 8, 12, 17, 19})
+    if (need <= mg) return mg;
+  return 0;
+}
+
+bool gn_fused_fits(long long N, int C_in, int C_out, int T_out, int dil, int cpg,
+                   const void* W) {
+  return T_out >= 1 && T_out <= 128 * GN_WAVES && dil <= 64 * GN_MG_MAX && C_in % GN_CI == 0 &&
+         C_out % 16 == 0 && cpg >= 1 && 16 % cpg == 0 && gn_fused_groups(T_out, dil) > 0 &&
+         (reinterpret_cast<uintptr_t>(W) & 7) == 0 && N * (C_out / 16) <= 0x7fffffffLL;
+}
+
+hipError_t launch_conv_gn_fused(const GnFusedArgs& a, hipStream_t stream) {
+  const long long nwg = (long long)a.N * a.n_cb;
+  if (nwg <= 0) return hipSuccess;
+  // the shape must be one the kernel's indexing covers (the host picks this path only then)
+  const int mg = gn_fused_groups(a.T_out, a.dil);
+  if (mg == 0 || a.mg != mg || a.T_out > 128 * GN_WAVES || a.C_in % GN_CI != 0 ||
+      a.n_cb * 16 != a.C_out || a.cpg < 1 || 16 % a.cpg != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nwg), block(64 * GN_WAVES);
+  switch (mg) {
+    case 4: hipLaunchKernelGGL(conv_gn_fused_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(conv_gn_fused_kernel<8>, grid, block, 0, stream, a); break;
+    case 12: hipLaunchKernelGGL(conv_gn_fused_kernel<12>, grid, block, 0, stream, a); break;
+    case 17: hipLaunchKernelGGL(conv_gn_fused_kernel<17>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(conv_gn_fused_kernel<19>, grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dconv1d

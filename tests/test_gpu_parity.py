@@ -233,6 +233,18 @@ GN_CASES = [
     (2, 64, 300, 150, 3, 1, 1, False, True),     # 128-channel tiles, 3 channel tiles
     (2, 96, 128, 2048, 8, 1, 1, True, True),     # 9 chunks (odd), T_out % 4 == 0
     (4, 32, 256, 1026, 16, 0, 1, False, True),   # 3 chunks (odd), T_out = 1024
+    # single-launch path (groups inside 16 channels, T_out <= 1024, C_in % 16 == 0, staged
+    # window 128*ceil(T_out/128) + 2*dil <= 1216 steps); the cases above with C_in of 8,
+    # 32 with T_out > 1024, 40, or 32 channels per group take the two-launch path:
+    (2, 48, 48, 200, 6, 1, 1, True, True),       # 3 input-channel chunks (odd)
+    (2, 16, 16, 1000, 8, 0, 1, False, True),     # one chunk, 2 channels per group
+    (3, 16, 16, 5, 4, 2, 3, True, True),         # T_out = 3
+    (1, 16, 32, 600, 16, 5, 200, True, True),    # taps 200 apart, pad != dil
+    (1, 16, 32, 1100, 4, 0, 256, False, True),   # pad 0, T_out = 588
+    (1, 16, 32, 1024, 2, 96, 96, True, False),   # widest staged window (1216 steps)
+    (1, 16, 32, 1024, 2, 97, 97, True, True),    # one step past it: two-launch path
+    (2, 16, 32, 100, 4, 3, 1, False, True),      # pad > dil
+    (3, 64, 256, 1024, 32, 1, 1, True, True),    # the GN workload's layer with a bias
 ]
 
 
