@@ -381,7 +381,8 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
 
   // Every group inside 16 output channels and T_out <= 1024: one launch, no workspace.
   const int cpg = (int)(C_out / num_groups);
-  if (gn_fused_fits(N, (int)C_in, (int)C_out, Lo, (int)dilation, cpg, W)) {
+  if (gn_fused_fits(N, (int)C_in, (int)C_out, (int)T, Lo, (int)padding, (int)dilation, cpg, x,
+                    W)) {
     GnFusedArgs g{};
     g.x = x;
     g.W = W;
@@ -398,7 +399,9 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
     g.pad = (int)padding;
     g.dil = (int)dilation;
     g.cpg = cpg;
-    g.mg = gn_fused_groups(Lo, (int)dilation);
+    g.vec4 = gn_fused_vec4((int)T, x) ? 1 : 0;
+    g.delta = gn_fused_delta((int)padding, g.vec4 != 0);
+    g.mg = gn_fused_groups(Lo, (int)dilation, g.delta);
     g.n_cb = (int)C_out / 16;
     const int slot = timer_begin(stream);
     hipError_t e = launch_conv_gn_fused(g, stream);

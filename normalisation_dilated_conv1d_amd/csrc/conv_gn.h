@@ -8,7 +8,9 @@ namespace dconv1d {
 
 // conv_gn.hip: Conv1d + GroupNorm in one launch when every group fits in a workgroup of
 // 16 output channels x T_out <= 1024 steps. The staged window is 64*mg steps wide
-// (gn_fused_groups; 0 when no instantiated width covers the shape).
+// (gn_fused_groups; 0 when no instantiated width covers the shape) and starts at input
+// step -pad - delta; x is staged with 16-byte loads when gn_fused_vec4, and then delta
+// (gn_fused_delta) aligns the window start to a multiple of 4.
 constexpr int GN_MG_MAX = 19;
 struct GnFusedArgs {
   const float* x;       // [N][C_in][T]
@@ -21,11 +23,16 @@ struct GnFusedArgs {
   int N, C_in, C_out, T, T_out;
   int pad, dil;         // tap k reads input t - pad + k*dil
   int cpg;              // channels per group (divides 16)
-  int mg;               // staged window width in 64-step groups, gn_fused_groups(T_out, dil)
+  int mg;               // staged window width in 64-step groups, gn_fused_groups(...)
+  int vec4;             // 16-byte x loads, gn_fused_vec4(T, x)
+  int delta;            // window start shift, gn_fused_delta(pad, vec4)
   int n_cb;             // C_out / 16
 };
-int gn_fused_groups(int T_out, int dil);
-bool gn_fused_fits(long long N, int C_in, int C_out, int T_out, int dil, int cpg, const void* W);
+int gn_fused_groups(int T_out, int dil, int delta);
+bool gn_fused_vec4(int T, const void* x);
+int gn_fused_delta(int pad, bool vec4);
+bool gn_fused_fits(long long N, int C_in, int C_out, int T, int T_out, int pad, int dil, int cpg,
+                   const void* x, const void* W);
 hipError_t launch_conv_gn_fused(const GnFusedArgs& a, hipStream_t stream);
 
 }  // namespace dconv1d

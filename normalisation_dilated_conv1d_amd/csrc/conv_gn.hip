@@ -17,13 +17,15 @@
 //                output step reads, once, into LDS: tap k of output step t reads window
 //                column t + k*dil, so the three taps share one staged copy and x crosses
 //                L2 -> LDS once per workgroup. Wave w stages channels 16c + w and
-//                16c + w + 8: MG buffer loads of 64 steps per channel into registers, two
-//                chunks ahead (chunk c + 2 loads
+//                16c + w + 8 with buffer loads into registers (16 bytes per lane when T
+//                is a multiple of 4 and x is 16-byte aligned, else 4), two chunks ahead (chunk c + 2 loads
 //                while chunk c computes; chunk c + 1, loaded during chunk c - 1, goes to
-//                LDS after chunk c's MFMAs), then one 256-byte ds_write per load. Steps
-//                outside [0, T) get an offset past the end of the row's buffer range, so
-//                the hardware range check delivers exact zeros. Two LDS buffers, one
-//                barrier per chunk. (Loads straight into LDS were tried: the compiler
+//                LDS after chunk c's MFMAs), then one ds_write per load. Steps outside
+//                [0, T) get an offset past the end of the row's buffer range, so the
+//                hardware range check delivers exact zeros; with 16-byte loads the window
+//                starts at the multiple of 4 at or below -pad (shift delta in 0..3), so a
+//                load lies entirely inside or entirely outside [0, T). Two LDS buffers,
+//                one barrier per chunk. (Loads straight into LDS were tried: the compiler
 //                then waits for every one of them before each LDS read.)
 //   LDS layout = row r (channel 16c + r) at r*RS floats, RS = 64*MG + 8: RS = 8 mod 16
 //                puts the rows 2lq of the four quarter-waves of a B read on different
@@ -31,13 +33,15 @@
 //   operands   = MFMA K-step (tap k, half g, e): quarter-wave lq = lane/16 supplies input
 //                channel 16c + 8g + 2lq + e. A = W[co0 + lane%16][16c + 8g + 2lq + e][k]:
 //                per half, six consecutive floats of the [C_out][C_in][3] layout per lane.
-//                B = window column t + k*dil of row 8g + 2lq + e. 96 MFMAs per wave per
+//                B = window column t + k*dil + delta of row 8g + 2lq + e. 96 MFMAs per wave per
 //                chunk between barriers.
 //   statistics = two passes over the registers: per-row sums (quarter-wave butterflies),
 //                then per group, in double, over (wave, row) in a fixed order -> mean;
 //                the same for the sum of squared deviations from that mean -> biased
 //                variance. Bitwise reproducible: no atomics, no order that depends on
 //                timing.
+
+#include <type_traits>
 
 #include "conv_gn.h"
 
@@ -71,8 +75,9 @@ __device__ __forceinline__ float quarterwave_sum(float v) {
 
 }  // namespace
 
-// MG: 64-step groups of the staged window (the window is 64*MG steps wide)
-template <int MG>
+// MG: 64-step groups of the staged window (the window is 64*MG steps wide); VW: floats
+// per lane per load (1 or 4)
+template <int MG, int VW>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * GN_WAVES, 64 * GN_WAVES)))
 conv_gn_fused_kernel(GnFusedArgs a) {
   constexpr int RS = 64 * MG + 8;             // floats per staged row
@@ -110,37 +115,52 @@ conv_gn_fused_kernel(GnFusedArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[nb][r] = 0.f;
 
-  // byte offset of window step 64m + l in its row: input step t = 64m + l - pad, or an
-  // offset the range check rejects (t < 0; t >= T is past the range by itself). Opaque,
-  // so that no constant part is folded into the instruction offset (which could bring a
-  // rejected offset back into range).
-  uint32_t voff[MG];
+  // Load i of a row covers window columns [64*VW*i + VW*l, +VW), input steps from
+  // ws = -pad - delta on. Its byte offset, or one the range check rejects (t < 0 or past
+  // the window; t >= T is past the row's range by itself). Opaque, so that no constant
+  // part is folded into the instruction offset (which could bring a rejected offset back
+  // into range).
+  static_assert(VW == 1 || VW == 4, "4- or 16-byte loads");
+  using XV = typename std::conditional<VW == 4, f32x4, float>::type;
+  constexpr int NL = (64 * MG + 64 * VW - 1) / (64 * VW);   // loads per row
+  const int ws = -a.pad - a.delta;
+  uint32_t voff[NL];
 #pragma unroll
-  for (int m = 0; m < MG; ++m) {
-    const int t = 64 * m + l - a.pad;
-    voff[m] = t >= 0 ? 4u * (uint32_t)t : kOutOfRange;
-    asm volatile("" : "+v"(voff[m]));
+  for (int i = 0; i < NL; ++i) {
+    const int j = 64 * VW * i + VW * l;
+    const int t = ws + j;
+    voff[i] = (t >= 0 && j < 64 * MG) ? 4u * (uint32_t)t : kOutOfRange;
+    asm volatile("" : "+v"(voff[i]));
   }
-  // this wave's rows of chunk c (channels 16c + w and 16c + w + 8): MG loads of 64
-  // steps each into registers
-  float xa[2][MG], xb[2][MG];
-  auto load_x = [&](int c, float (&dst)[2][MG]) {
+  // this wave's rows of chunk c (channels 16c + w and 16c + w + 8) into registers
+  XV xa[2][NL], xb[2][NL];
+  auto load_x = [&](int c, XV (&dst)[2][NL]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(xn + (size_t)(GN_CI * c + w + 8 * h) * a.T), (short)0, 4 * a.T,
           kBufferFlags);
 #pragma unroll
-      for (int m = 0; m < MG; ++m)
-        dst[h][m] =
-            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff[m], 0, 0));
+      for (int i = 0; i < NL; ++i) {
+        if constexpr (VW == 4)
+          dst[h][i] =
+              __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, 0));
+        else
+          dst[h][i] =
+              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], 0, 0));
+      }
     }
   };
-  auto store_x = [&](const float (&src)[2][MG], float* zb) {
+  // window columns past 64*MG (the tail of the last 16-byte load) are not stored
+  auto store_x = [&](const XV (&src)[2][NL], float* zb) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int m = 0; m < MG; ++m) zb[(w + 8 * h) * RS + 64 * m + l] = src[h][m];
+      for (int i = 0; i < NL; ++i) {
+        const int j = 64 * VW * i + VW * l;
+        if (64 * VW * (i + 1) <= 64 * MG || j < 64 * MG)
+          *reinterpret_cast<XV*>(zb + (w + 8 * h) * RS + j) = src[h][i];
+      }
   };
   const int nC = a.C_in / GN_CI;
   // A operands of chunk c: W[co0 + l16][16c + 8g + 2lq + e][k] at wrow + 48c + 24g + 3e + k,
@@ -158,8 +178,8 @@ conv_gn_fused_kernel(GnFusedArgs a) {
       }
     }
   };
-  // B operand base of this lane: row 2lq, window column tw + l16
-  const int boff = 2 * lq * RS + tw + l16;
+  // B operand base of this lane: row 2lq, window column tw + l16 + delta
+  const int boff = 2 * lq * RS + tw + l16 + a.delta;
   // the chunk's 96 MFMAs of this wave on buffer zb, in six steps (tap k, half g); the B
   // operands of the next step are read while the current step's MFMAs run
   auto compute = [&](const float* zb, const float (&wv)[12]) {
@@ -193,7 +213,7 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   // computes from buffer zc, then chunk c + 1's row (loaded a chunk ago) goes to buffer zn
   // (last read by chunk c - 1, which every wave finished before the previous barrier)
   auto chunk = [&](int c, const float* zc, float* zn, const float (&wc)[12], float (&w1)[12],
-                   float (&x2)[2][MG], const float (&x1)[2][MG]) {
+                   XV (&x2)[2][NL], const XV (&x1)[2][NL]) {
     load_w(c + 1, w1);
     load_x(min(c + 2, nC - 1), x2);
     __builtin_amdgcn_sched_barrier(0);
@@ -290,37 +310,54 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   }
 }
 
-int gn_fused_groups(int T_out, int dil) {
-  const long long span = 128LL * ((T_out + 127) / 128) + 2LL * dil;
+int gn_fused_groups(int T_out, int dil, int delta) {
+  const long long span = 128LL * ((T_out + 127) / 128) + 2LL * dil + delta;
   const int need = (int)((span + 63) / 64);
   for (int mg : {4, 8, 12, 17, 19})
     if (need <= mg) return mg;
   return 0;
 }
 
-bool gn_fused_fits(long long N, int C_in, int C_out, int T_out, int dil, int cpg,
-                   const void* W) {
+bool gn_fused_vec4(int T, const void* x) {
+  return T % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+}
+
+int gn_fused_delta(int pad, bool vec4) { return vec4 ? (4 - pad % 4) % 4 : 0; }
+
+bool gn_fused_fits(long long N, int C_in, int C_out, int T, int T_out, int pad, int dil, int cpg,
+                   const void* x, const void* W) {
+  const int delta = gn_fused_delta(pad, gn_fused_vec4(T, x));
   return T_out >= 1 && T_out <= 128 * GN_WAVES && dil <= 64 * GN_MG_MAX && C_in % GN_CI == 0 &&
-         C_out % 16 == 0 && cpg >= 1 && 16 % cpg == 0 && gn_fused_groups(T_out, dil) > 0 &&
+         C_out % 16 == 0 && cpg >= 1 && 16 % cpg == 0 && gn_fused_groups(T_out, dil, delta) > 0 &&
          (reinterpret_cast<uintptr_t>(W) & 7) == 0 && N * (C_out / 16) <= 0x7fffffffLL;
+}
+
+template <int VW>
+static void launch_mg(const GnFusedArgs& a, int mg, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (mg) {
+    case 4: hipLaunchKernelGGL((conv_gn_fused_kernel<4, VW>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((conv_gn_fused_kernel<8, VW>), grid, block, 0, stream, a); break;
+    case 12: hipLaunchKernelGGL((conv_gn_fused_kernel<12, VW>), grid, block, 0, stream, a); break;
+    case 17: hipLaunchKernelGGL((conv_gn_fused_kernel<17, VW>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((conv_gn_fused_kernel<19, VW>), grid, block, 0, stream, a); break;
+  }
 }
 
 hipError_t launch_conv_gn_fused(const GnFusedArgs& a, hipStream_t stream) {
   const long long nwg = (long long)a.N * a.n_cb;
   if (nwg <= 0) return hipSuccess;
   // the shape must be one the kernel's indexing covers (the host picks this path only then)
-  const int mg = gn_fused_groups(a.T_out, a.dil);
-  if (mg == 0 || a.mg != mg || a.T_out > 128 * GN_WAVES || a.C_in % GN_CI != 0 ||
-      a.n_cb * 16 != a.C_out || a.cpg < 1 || 16 % a.cpg != 0)
+  const bool v4 = gn_fused_vec4(a.T, a.x);
+  const int mg = gn_fused_groups(a.T_out, a.dil, a.delta);
+  if (mg == 0 || a.mg != mg || a.vec4 != (int)v4 || a.delta != gn_fused_delta(a.pad, v4) ||
+      a.T_out > 128 * GN_WAVES || a.C_in % GN_CI != 0 || a.n_cb * 16 != a.C_out || a.cpg < 1 ||
+      16 % a.cpg != 0)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(64 * GN_WAVES);
-  switch (mg) {
-    case 4: hipLaunchKernelGGL(conv_gn_fused_kernel<4>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(conv_gn_fused_kernel<8>, grid, block, 0, stream, a); break;
-    case 12: hipLaunchKernelGGL(conv_gn_fused_kernel<12>, grid, block, 0, stream, a); break;
-    case 17: hipLaunchKernelGGL(conv_gn_fused_kernel<17>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(conv_gn_fused_kernel<19>, grid, block, 0, stream, a); break;
-  }
+  if (v4)
+    launch_mg<4>(a, mg, grid, block, stream);
+  else
+    launch_mg<1>(a, mg, grid, block, stream);
   return hipGetLastError();
 }
 

@@ -245,6 +245,7 @@ GN_CASES = [
     (1, 16, 32, 1024, 2, 97, 97, True, True),    # one step past it: two-launch path
     (2, 16, 32, 100, 4, 3, 1, False, True),      # pad > dil
     (3, 64, 256, 1024, 32, 1, 1, True, True),    # the GN workload's layer with a bias
+    (2, 32, 64, 512, 8, 2, 2, False, True),      # window shift 2 (16-byte loads)
 ]
 
 
@@ -271,6 +272,24 @@ def test_groupnorm_matches_oracle(N, C_in, C_out, T, G, pad, dil, bias, affine):
         p["beta"] = None
     got = run_gn(p, G, pad, dil).cpu().numpy()
     err = maxrel(got, oracle_gn(p, G, pad, dil))
+    assert err <= TOL_F32, err
+
+
+def test_groupnorm_unaligned_x():
+    """x only 4-byte aligned (a view one float into a buffer): the single-launch path
+    then stages with 4-byte loads; same bar against the oracle."""
+    N, C_in, C_out, T, G, pad, dil = 2, 32, 64, 512, 8, 1, 1
+    announce("conv1d_groupnorm_fwd unaligned x", (N, C_in, C_out, T, G, pad, dil))
+    p = groupnorm_inputs(N, C_in, C_out, T, 30_777, with_bias=True)
+    q = to_dev(p)
+    buf = torch.empty(N * C_in * T + 4, device="cuda")
+    x = buf[1:1 + N * C_in * T].view(N, C_in, T)
+    x.copy_(q["x"])
+    assert x.data_ptr() % 16 != 0
+    got = dc.conv1d_groupnorm_fwd(x, q["W"], q["bias"], q["gamma"], q["beta"], q["eps"], G,
+                                  pad, dil)
+    torch.cuda.synchronize()
+    err = maxrel(got.cpu().numpy(), oracle_gn(p, G, pad, dil))
     assert err <= TOL_F32, err
 
 
