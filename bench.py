@@ -28,12 +28,15 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
-# committed PMC traffic records of the dominant kernel, per block workload (eval-mode BN)
+# committed PMC traffic records of the dominant kernel, per workload (eval-mode BN for the
+# block workloads)
 TRAFFIC_FILES = {
     1: ("conv_f32_kernel", os.path.join(ROOT, "profiles",
                                         "traffic_conv_f32_prenorm_N32_C256_L4096_d128.json")),
     4: ("conv_bf16_kernel", os.path.join(ROOT, "profiles",
                                          "traffic_conv_bf16_prenorm_N16_C512_L16384_d128.json")),
+    3: ("conv_gn_fused_kernel",
+        os.path.join(ROOT, "profiles", "traffic_conv_gn_fused_N16_Cin128_Cout256_T1024_G32.json")),
 }
 
 

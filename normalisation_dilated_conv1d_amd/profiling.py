@@ -37,6 +37,9 @@ KERNEL_SOURCES = {
                         "normalisation_dilated_conv1d_amd/csrc/internal.h"],
     "conv_bf16_kernel": ["normalisation_dilated_conv1d_amd/csrc/conv_bf16.hip",
                          "normalisation_dilated_conv1d_amd/csrc/internal.h"],
+    "conv_gn_fused_kernel": ["normalisation_dilated_conv1d_amd/csrc/conv_gn.hip",
+                             "normalisation_dilated_conv1d_amd/csrc/conv_gn.h",
+                             "normalisation_dilated_conv1d_amd/csrc/internal.h"],
 }
 
 

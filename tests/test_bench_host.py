@@ -23,8 +23,14 @@ def test_more_than_one_gpu_exits_with_message():
 
 
 def test_traffic_unknown_workload_is_none():
-    assert bench.measured_traffic(3) is None
     assert bench.measured_traffic(0) is None
+    assert bench.measured_traffic(2) is None
+
+
+def test_traffic_committed_records_match_sources():
+    """Every committed traffic record describes the kernel source as it is now."""
+    for workload in sorted(bench.TRAFFIC_FILES):
+        assert bench.measured_traffic(workload) is not None, workload
 
 
 @pytest.mark.parametrize("workload", sorted(bench.TRAFFIC_FILES))
