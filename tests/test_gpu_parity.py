@@ -246,6 +246,7 @@ GN_CASES = [
     (2, 16, 32, 100, 4, 3, 1, False, True),      # pad > dil
     (3, 64, 256, 1024, 32, 1, 1, True, True),    # the GN workload's layer with a bias
     (2, 32, 64, 512, 8, 2, 2, False, True),      # window shift 2 (16-byte loads)
+    (40, 32, 128, 256, 16, 1, 1, True, True),    # 320 workgroups: more than one per CU
 ]
 
 
