@@ -13,28 +13,29 @@
 //   waves      = 8; wave w owns output steps [128w, 128w + 128): 8 accumulator blocks of
 //                16 x 16 (v_mfma_f32_16x16x4_f32, float32 products and accumulation).
 //   K loop     = chunks of 16 input channels. A chunk stages x[n][16c .. 16c + 16) over the
-//                window of input steps [-pad, -pad + 64*MG) that every tap of every
-//                output step reads, once, into LDS: tap k of output step t reads window
-//                column t + k*dil, so the three taps share one staged copy and x crosses
-//                L2 -> LDS once per workgroup. Wave w stages channels 16c + w and
-//                16c + w + 8 with buffer loads into registers (16 bytes per lane when T
-//                is a multiple of 4 and x is 16-byte aligned, else 4), two chunks ahead (chunk c + 2 loads
-//                while chunk c computes; chunk c + 1, loaded during chunk c - 1, goes to
-//                LDS after chunk c's MFMAs), then one ds_write per load. Steps outside
-//                [0, T) get an offset past the end of the row's buffer range, so the
-//                hardware range check delivers exact zeros; with 16-byte loads the window
-//                starts at the multiple of 4 at or below -pad (shift delta in 0..3), so a
-//                load lies entirely inside or entirely outside [0, T). Two LDS buffers,
-//                one barrier per chunk. (Loads straight into LDS were tried: the compiler
-//                then waits for every one of them before each LDS read.)
+//                window of input steps [ws, ws + 64*MG), ws = -pad - delta, that every tap
+//                of every output step reads, once, into LDS: tap k of output step t reads
+//                window column t + k*dil + delta, so the three taps share one staged copy
+//                and x crosses L2 -> LDS once per workgroup. Wave w stages channels
+//                16c + w and 16c + w + 8 with buffer loads into registers (16 bytes per
+//                lane when T is a multiple of 4 and x is 16-byte aligned, else 4), two
+//                chunks ahead (chunk c + 2 loads while chunk c computes; chunk c + 1,
+//                loaded during chunk c - 1, goes to LDS after chunk c's MFMAs), then one
+//                ds_write per load. Steps outside [0, T) get an offset past the end of the
+//                row's buffer range, so the hardware range check delivers exact zeros.
+//                With 16-byte loads delta (0..3) puts ws on a multiple of 4, so a load lies
+//                entirely inside or entirely outside [0, T); with 4-byte loads delta = 0.
+//                Two LDS buffers, one barrier per chunk. (Loads straight into LDS were
+//                tried: the compiler then waits for every one of them before each LDS
+//                read.)
 //   LDS layout = row r (channel 16c + r) at r*RS floats, RS = 64*MG + 8: RS = 8 mod 16
 //                puts the rows 2lq of the four quarter-waves of a B read on different
 //                banks.
 //   operands   = MFMA K-step (tap k, half g, e): quarter-wave lq = lane/16 supplies input
 //                channel 16c + 8g + 2lq + e. A = W[co0 + lane%16][16c + 8g + 2lq + e][k]:
 //                per half, six consecutive floats of the [C_out][C_in][3] layout per lane.
-//                B = window column t + k*dil + delta of row 8g + 2lq + e. 96 MFMAs per wave per
-//                chunk between barriers.
+//                B = window column t + k*dil + delta of row 8g + 2lq + e. 96 MFMAs per
+//                wave per chunk between barriers.
 //   statistics = two passes over the registers: per-row sums (quarter-wave butterflies),
 //                then per group, in double, over (wave, row) in a fixed order -> mean;
 //                the same for the sum of squared deviations from that mean -> biased
@@ -106,7 +107,7 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   const bool active = tw < a.T_out;       // waves past the end only stage
 
   const float* xn = a.x + (size_t)n * a.C_in * a.T;
-  // lane's A operands of chunk c: W[co0 + l16][8c + 2lq + e][k] at wrow + 24c + 3e + k
+  // this lane's weight row: W[co0 + l16][2lq][0] (see load_w)
   const float* __restrict__ wrow = a.W + ((size_t)(co0 + l16) * a.C_in + 2 * lq) * 3;
 
   f32x4 acc[GN_NB];
