@@ -4,6 +4,11 @@
         Markdown table of per-kernel call counts and durations from a
         ``rocprofv3 --kernel-trace --stats --output-format csv`` run.
 
+    python -m normalisation_dilated_conv1d_amd.profiling warm KERNEL_TRACE_CSV --kernel NAME
+        Average and median duration of one kernel's dispatches in a ``--kernel-trace`` run,
+        leaving out the dispatches that follow bench.py's cache-flush fill kernel (reported
+        separately).
+
     python -m normalisation_dilated_conv1d_amd.profiling traffic \\
         --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel conv_f32_kernel \\
         --calib-mib 192 --out profiles/traffic_....json --cmd-fetch "..." --cmd-write "..."
@@ -71,6 +76,35 @@ def stats_markdown(path: str, cmd: str) -> str:
         pct = float(r.get("Percentage", 0))
         out.append(f"| `{name[:90]}` | {calls} | {tot:.1f} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f}% |")
     return "Command:\n\n```\n" + cmd + "\n```\n\n" + "\n".join(out) + "\n"
+
+
+def warm_split(trace_csv: str, kernel: str):
+    """Durations (us) of the dispatches of `kernel` in a ``--kernel-trace`` CSV, split into
+    warm ones and cold ones (those with a fill kernel since the kernel's previous dispatch:
+    bench.py's cold-cache pass overwrites a scratch buffer before each such step)."""
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    warm, cold = [], []
+    flushed = False
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "FillFunctor" in name:
+            flushed = True
+        elif kernel in name:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            (cold if flushed else warm).append(d)
+            flushed = False
+    return warm, cold
+
+
+def warm_markdown(trace_csv: str, kernel: str) -> str:
+    warm, cold = warm_split(trace_csv, kernel)
+    if not warm:
+        raise SystemExit(f"kernel {kernel} not found in {trace_csv}")
+    out = [f"`{kernel}` per dispatch: {len(warm)} warm, average {statistics.mean(warm):.2f} us, "
+           f"median {statistics.median(warm):.2f} us"]
+    if cold:
+        out.append(f"; {len(cold)} after a cache flush, average {statistics.mean(cold):.2f} us")
+    return "".join(out) + ".\n"
 
 
 def _per_dispatch(rows, counter):
@@ -163,6 +197,9 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    wsub = sub.add_parser("warm")
+    wsub.add_argument("trace_csv")
+    wsub.add_argument("--kernel", required=True)
     m = sub.add_parser("mfma")
     m.add_argument("csv")
     m.add_argument("--kernel", required=True)
@@ -171,6 +208,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.what == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.cmd))
+    elif a.what == "warm":
+        sys.stdout.write(warm_markdown(a.trace_csv, a.kernel))
     elif a.what == "mfma":
         sys.stdout.write(mfma_markdown(a.csv, a.kernel, a.algorithmic_flops, a.cmd))
     else:
