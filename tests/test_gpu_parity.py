@@ -277,20 +277,28 @@ def test_groupnorm_matches_oracle(N, C_in, C_out, T, G, pad, dil, bias, affine):
 
 
 def test_groupnorm_unaligned_x():
-    """x only 4-byte aligned (a view one float into a buffer): the single-launch path
-    then stages with 4-byte loads; same bar against the oracle."""
+    """x and out only 4-byte aligned (views one float into buffers): the single-launch path
+    then stages with 4-byte loads; same bar against the oracle, and the floats around out
+    stay untouched."""
     N, C_in, C_out, T, G, pad, dil = 2, 32, 64, 512, 8, 1, 1
-    announce("conv1d_groupnorm_fwd unaligned x", (N, C_in, C_out, T, G, pad, dil))
+    announce("conv1d_groupnorm_fwd unaligned x and out", (N, C_in, C_out, T, G, pad, dil))
     p = groupnorm_inputs(N, C_in, C_out, T, 30_777, with_bias=True)
     q = to_dev(p)
     buf = torch.empty(N * C_in * T + 4, device="cuda")
     x = buf[1:1 + N * C_in * T].view(N, C_in, T)
     x.copy_(q["x"])
     assert x.data_ptr() % 16 != 0
-    got = dc.conv1d_groupnorm_fwd(x, q["W"], q["bias"], q["gamma"], q["beta"], q["eps"], G,
-                                  pad, dil)
+    T_out = T + 2 * pad - 2 * dil
+    n_out = N * C_out * T_out
+    obuf = torch.full((n_out + 8,), 12345.0, device="cuda")
+    out = obuf[1:1 + n_out].view(N, C_out, T_out)
+    assert out.data_ptr() % 16 != 0
+    dc.conv1d_groupnorm_fwd(x, q["W"], q["bias"], q["gamma"], q["beta"], q["eps"], G, pad, dil,
+                            out=out)
     torch.cuda.synchronize()
-    err = maxrel(got.cpu().numpy(), oracle_gn(p, G, pad, dil))
+    ob = obuf.cpu()
+    assert ob[0] == 12345.0 and torch.all(ob[1 + n_out:] == 12345.0)
+    err = maxrel(out.cpu().numpy(), oracle_gn(p, G, pad, dil))
     assert err <= TOL_F32, err
 
 
