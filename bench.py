@@ -6,10 +6,11 @@ workload: the BN fold + weight repack kernel and the fused implicit-GEMM kernel,
 all inputs resident in HBM. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--workload 1|3|4]
+                    [--workload 1|2|3|4] [--dilation D]
 
---workload 3 (Conv1d+GroupNorm) and 4 (bf16 storage) time the other workloads the same
-way; the default, workload 1, is the reported metric. For the block workloads,
+--workload 2 (the same block at dilation D, one of 1, 8, 512, 2048), 3 (Conv1d+GroupNorm)
+and 4 (bf16 storage) time the other workloads the same way; the default, workload 1, is
+the reported metric. For the block workloads,
 --bn train times the training-mode entry point (batch-statistics pass, running-stat
 update, then the same conv) and --bn external the entry point that takes an already
 normalised input and a separate residual.
@@ -108,17 +109,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
-    ap.add_argument("--workload", type=int, default=1, choices=(1, 3, 4),
+    ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 3, 4),
                     help="1: fp32 block N32 C256 L4096 d128 (default, the reported metric); "
+                         "2: the same block at --dilation D (1, 8, 512 or 2048); "
                          "3: Conv1d+GroupNorm N16 Cin128 Cout256 T1024 G32; "
                          "4: bf16-storage block N16 C512 L16384 d128")
+    ap.add_argument("--dilation", type=int, default=None,
+                    help="workload 2: the dilation (= padding) of the sweep to time")
     ap.add_argument("--bn", default="eval", choices=("eval", "train", "external"),
                     help="block workloads: BatchNorm in eval mode (default), training mode, "
                          "or done by the caller (ReLU + conv + separate residual)")
     args = ap.parse_args()
 
     if args.bn != "eval" and args.workload == 3:
-        ap.error("--bn applies to the block workloads (1 and 4)")
+        ap.error("--bn applies to the block workloads (1, 2 and 4)")
+    if (args.dilation is not None) != (args.workload == 2):
+        ap.error("--dilation goes with --workload 2, and workload 2 needs it")
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (the "
               "block would shard over the batch with no exchange between GPUs)",
@@ -133,12 +139,19 @@ def main():
 
     wl = WORKLOADS[args.workload]
     w = wl.dims
+    wname = wl.name if args.workload != 2 else f"{wl.name}_d{args.dilation}"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if wl.kind == "prenorm":
+        if args.workload == 2:
+            if args.dilation not in w["ds"]:
+                ap.error(f"--dilation must be one of {w['ds']}")
+            w = dict(w, d=args.dilation)
         N, C, L, d = w["N"], w["C"], w["L"], w["d"]
         bf16 = w["dtype"] == "bf16"
-        p = prenorm_inputs(N, C, L, seed_for(args.workload), bf16=bf16)
+        # the sweep's inputs are drawn per dilation, as in its parity tests
+        p = prenorm_inputs(N, C, L, seed_for(args.workload, d if args.workload == 2 else 0),
+                           bf16=bf16)
         q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
         out = torch.empty_like(q["x"])
         if args.bn == "eval":
@@ -174,8 +187,12 @@ def main():
             # train: the statistics pass reads x before the conv can start; external: the
             # normalised input and the residual are separate tensors
             alg_bytes += esz * 1.0 * N * C * L
-        config = {"workload": wl.name, "N": N, "C": C, "L": L, "kernel_size": 3,
+        config = {"workload": wname, "N": N, "C": C, "L": L, "kernel_size": 3,
                   "dilation": d, "padding": d, "bn_mode": args.bn, "parallelism": "single GPU"}
+        if args.workload == 2:
+            # share of the counted (output step, tap) pairs whose input lies inside [0, L);
+            # the metric counts the padded ones too
+            config["valid_tap_share"] = round((L + 2 * max(L - d, 0)) / (3 * L), 4)
         kernel_name = ("conv_bf16_kernel<pair>" if bf16
                        else "conv_f32_kernel<128, BN, residual, float>")
     else:
@@ -258,8 +275,8 @@ def main():
     k_tflops = flops / (kern_ms_avg * 1e-3) / 1e12
     metric = ("fused block TFLOP/s & GB/s (N32 C256 L4096 d128) vs MI355X roofline"
               if args.workload == 1 and args.bn == "eval"
-              else f"TFLOP/s & GB/s, {wl.name}, BN {args.bn}, vs MI355X roofline"
-              if wl.kind == "prenorm" else f"TFLOP/s & GB/s, {wl.name}, vs MI355X roofline")
+              else f"TFLOP/s & GB/s, {wname}, BN {args.bn}, vs MI355X roofline"
+              if wl.kind == "prenorm" else f"TFLOP/s & GB/s, {wname}, vs MI355X roofline")
 
     line = {
         "metric": metric,
