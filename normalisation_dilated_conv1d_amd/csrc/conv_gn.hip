@@ -37,7 +37,8 @@
 //                B = window column t + k*dil + delta of row 8g + 2lq + e. 96 MFMAs per
 //                wave per chunk between barriers.
 //   statistics = two passes over the registers: per-row sums (quarter-wave butterflies),
-//                then per group, in double, over (wave, row) in a fixed order -> mean;
+//                then per group, in double, over (wave, row) in a fixed butterfly order
+//                across one wave's lanes -> mean;
 //                the same for the sum of squared deviations from that mean -> biased
 //                variance. Bitwise reproducible: no atomics, no order that depends on
 //                timing.
@@ -71,6 +72,19 @@ __device__ __forceinline__ float quarterwave_sum(float v) {
   v += swz_xor<4>(v);
   v += swz_xor<2>(v);
   v += swz_xor<1>(v);
+  return v;
+}
+
+// Sum, in double, of a group's per-(wave, row) partials red[16*ww + row] (8 waves x 16
+// rows; the group of row r is r / cpg), over the 64 lanes of one wave in a fixed order:
+// lane l adds the partials of waves l/16 and l/16 + 4 at row l%16, then butterflies over
+// the row bits below cpg and over the wave bits. Every lane ends with the total of the
+// group of row l%16; the order of additions does not depend on timing.
+__device__ __forceinline__ double group_total(const float* red, int l, int cpg) {
+  double v = (double)red[l] + (double)red[l + 64];
+  for (int m = 1; m < cpg; m <<= 1) v += __shfl_xor(v, m);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   return v;
 }
 
@@ -238,7 +252,6 @@ conv_gn_fused_kernel(GnFusedArgs a) {
 
   // Epilogue. Register r of block nb holds channel co0 + 4lq + r, step tw + 16nb + l16.
   const int cpg = a.cpg;
-  const int ngr = 16 / cpg;   // groups in this workgroup
   const double cnt = (double)cpg * (double)a.T_out;
   float y[GN_NB][4];
   bool valid[GN_NB];
@@ -261,11 +274,9 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     if (l16 == 0) red[w * 16 + 4 * lq + r] = s;
   }
   __syncthreads();
-  if (tid < ngr) {
-    double tot = 0.0;
-    for (int ww = 0; ww < GN_WAVES; ++ww)
-      for (int i = 0; i < cpg; ++i) tot += (double)red[ww * 16 + tid * cpg + i];
-    gmean[tid] = (float)(tot / cnt);
+  if (w == 0) {
+    const double tot = group_total(red, l, cpg);
+    if (l < 16 && l % cpg == 0) gmean[l / cpg] = (float)(tot / cnt);
   }
   __syncthreads();
 
@@ -286,11 +297,9 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     if (l16 == 0) red[w * 16 + 4 * lq + r] = s;
   }
   __syncthreads();
-  if (tid < ngr) {
-    double tot = 0.0;
-    for (int ww = 0; ww < GN_WAVES; ++ww)
-      for (int i = 0; i < cpg; ++i) tot += (double)red[ww * 16 + tid * cpg + i];
-    grstd[tid] = (float)(1.0 / sqrt(tot / cnt + (double)a.eps));
+  if (w == 0) {
+    const double tot = group_total(red, l, cpg);
+    if (l < 16 && l % cpg == 0) grstd[l / cpg] = (float)(1.0 / sqrt(tot / cnt + (double)a.eps));
   }
   __syncthreads();
 
