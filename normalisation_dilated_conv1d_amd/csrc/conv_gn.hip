@@ -36,11 +36,12 @@
 //                per half, six consecutive floats of the [C_out][C_in][3] layout per lane.
 //                B = window column t + k*dil + delta of row 8g + 2lq + e. 96 MFMAs per
 //                wave per chunk between barriers.
-//   statistics = two passes over the registers: per-row sums (quarter-wave butterflies),
-//                then per group, in double, over (wave, row) in a fixed butterfly order
-//                across one wave's lanes -> mean;
-//                the same for the sum of squared deviations from that mean -> biased
-//                variance. Bitwise reproducible: no atomics, no order that depends on
+//   statistics = two passes over the registers: per-row sums (DPP row rotations over each
+//                quarter-wave), then per group, in double, over (wave, row) in a fixed
+//                butterfly order across a wave's lanes -> mean; the same for the sum of
+//                squared deviations from that mean -> biased variance. Every wave forms
+//                the group totals itself, in the same order, so each pass needs one
+//                barrier. Bitwise reproducible: no atomics, no order that depends on
 //                timing.
 
 #include <type_traits>
@@ -62,16 +63,20 @@ constexpr int kBufferFlags = 0x00020000;
 // voffset that fails the range check of any row (rows are < 2^31 bytes)
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int XOR>
-__device__ __forceinline__ float swz_xor(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (XOR << 10) | 0x1F));
+// v of the lane K places further along its DPP row of 16 lanes (row_ror:K)
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 | K, 0xF, 0xF, false));
 }
-// sum over the 16 lanes of each quarter-wave; every lane ends with the same value
+// sum over the 16 lanes of each quarter-wave (a DPP row), with VALU row rotations rather
+// than LDS swizzles; every lane ends with the sum (lanes associate the terms differently,
+// so only one lane's value is used: the first lane of the row, always the same one)
 __device__ __forceinline__ float quarterwave_sum(float v) {
-  v += swz_xor<8>(v);
-  v += swz_xor<4>(v);
-  v += swz_xor<2>(v);
-  v += swz_xor<1>(v);
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
   return v;
 }
 
@@ -99,8 +104,8 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   constexpr int BUF = GN_CI * RS;             // floats per chunk buffer
   __shared__ __attribute__((aligned(16))) float zA[BUF];
   __shared__ __attribute__((aligned(16))) float zB[BUF];
-  __shared__ float red[GN_WAVES * 16];   // per (wave, row) partial of the current pass
-  __shared__ float gmean[16], grstd[16];
+  __shared__ float red[GN_WAVES * 16];    // per (wave, row) partials: sums
+  __shared__ float red2[GN_WAVES * 16];   // and sums of squared deviations
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -264,7 +269,9 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     for (int nb = 0; nb < GN_NB; ++nb) y[nb][r] = acc[nb][r] + bco;
   }
 
-  // pass 1: the group means
+  // pass 1: the group means. Every wave adds up the same partials in the same order
+  // (group_total), so no further barrier is needed to share the result; lane l ends with
+  // the total of the group of row l % 16, and a lane takes its rows' from lanes 0..15.
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float s = 0.f;
@@ -274,17 +281,13 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     if (l16 == 0) red[w * 16 + 4 * lq + r] = s;
   }
   __syncthreads();
-  if (w == 0) {
-    const double tot = group_total(red, l, cpg);
-    if (l < 16 && l % cpg == 0) gmean[l / cpg] = (float)(tot / cnt);
-  }
-  __syncthreads();
-
-  // pass 2: the biased variances, from the deviations about those means
+  const float gm = (float)(group_total(red, l, cpg) / cnt);
   float mean[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) mean[r] = gmean[(4 * lq + r) / cpg];
-  // (the barrier above also ends the pass-1 reads of red, so red can be rewritten)
+  for (int r = 0; r < 4; ++r) mean[r] = __shfl(gm, 4 * lq + r);
+
+  // pass 2: the biased variances, from the deviations about those means (into a second
+  // partials array: other waves may still be reading the first)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float s = 0.f;
@@ -294,14 +297,13 @@ conv_gn_fused_kernel(GnFusedArgs a) {
       s += valid[nb] ? dv * dv : 0.f;
     }
     s = quarterwave_sum(s);
-    if (l16 == 0) red[w * 16 + 4 * lq + r] = s;
+    if (l16 == 0) red2[w * 16 + 4 * lq + r] = s;
   }
   __syncthreads();
-  if (w == 0) {
-    const double tot = group_total(red, l, cpg);
-    if (l < 16 && l % cpg == 0) grstd[l / cpg] = (float)(1.0 / sqrt(tot / cnt + (double)a.eps));
-  }
-  __syncthreads();
+  const float gr = (float)(1.0 / sqrt(group_total(red2, l, cpg) / cnt + (double)a.eps));
+  float rstd[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rstd[r] = __shfl(gr, 4 * lq + r);
 
   // normalise and store: out = (y - mean) * rstd * gamma + beta
   float* __restrict__ outn = a.out + (size_t)n * a.C_out * a.T_out;
@@ -310,7 +312,7 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     const int co = co0 + 4 * lq + r;
     const float ga = a.gamma ? a.gamma[co] : 1.f;
     const float be = a.beta ? a.beta[co] : 0.f;
-    const float sc = grstd[(4 * lq + r) / cpg] * ga;
+    const float sc = rstd[r] * ga;
     float* __restrict__ orow = outn + (size_t)co * a.T_out;
 #pragma unroll
     for (int nb = 0; nb < GN_NB; ++nb) {
