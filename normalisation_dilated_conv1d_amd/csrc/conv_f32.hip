@@ -271,9 +271,12 @@ conv_f32_kernel(ConvF32Args a) {
           f32x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = v[e] + bia[i] + rv[i][e];
-          // t and L_out are multiples of 4: the 4 steps are all in range or all out
+          // t and L_out are multiples of 4: the 4 steps are all in range or all out.
+          // Non-temporal: out is not read again here, and the stores then pass the
+          // caches without allocating, which shortens the end-of-round write bursts.
           if (co < a.C_out && t < a.L_out)
-            *reinterpret_cast<f32x4*>(outn + (size_t)co * a.L_out + t) = o;
+            __builtin_nontemporal_store(
+                o, reinterpret_cast<f32x4*>(outn + (size_t)co * a.L_out + t));
         }
       }
     } else
@@ -300,7 +303,8 @@ conv_f32_kernel(ConvF32Args a) {
         for (int nb = 0; nb < NB; ++nb) {
           const int t = t0 + 16 * nb + l16;
           if (co < a.C_out && t < a.L_out)
-            from_f32(acc[mb][nb][r] + bco[r] + res[r][nb], &outn[co * a.L_out + t]);
+            __builtin_nontemporal_store(acc[mb][nb][r] + bco[r] + res[r][nb],
+                                        &outn[co * a.L_out + t]);
         }
       }
     }

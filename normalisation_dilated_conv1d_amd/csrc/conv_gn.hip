@@ -317,7 +317,8 @@ conv_gn_fused_kernel(GnFusedArgs a) {
 #pragma unroll
     for (int nb = 0; nb < GN_NB; ++nb) {
       const int t = tw + 16 * nb + l16;
-      if (valid[nb]) orow[t] = fmaf(y[nb][r] - mean[r], sc, be);
+      // non-temporal: out is not read again here, and all workgroups write it at once
+      if (valid[nb]) __builtin_nontemporal_store(fmaf(y[nb][r] - mean[r], sc, be), &orow[t]);
     }
   }
 }
