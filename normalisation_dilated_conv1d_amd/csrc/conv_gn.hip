@@ -313,12 +313,41 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     const float ga = a.gamma ? a.gamma[co] : 1.f;
     const float be = a.beta ? a.beta[co] : 0.f;
     const float sc = rstd[r] * ga;
-    float* __restrict__ orow = outn + (size_t)co * a.T_out;
 #pragma unroll
-    for (int nb = 0; nb < GN_NB; ++nb) {
-      const int t = tw + 16 * nb + l16;
-      // non-temporal: out is not read again here, and all workgroups write it at once
-      if (valid[nb]) __builtin_nontemporal_store(fmaf(y[nb][r] - mean[r], sc, be), &orow[t]);
+    for (int nb = 0; nb < GN_NB; ++nb) y[nb][r] = fmaf(y[nb][r] - mean[r], sc, be);
+  }
+  // Non-temporal stores: out is not read again here, and all workgroups write it at once.
+  const bool vec_out = (a.T_out & 3) == 0 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
+  if (vec_out) {
+    // Through the idle staging buffer zA, so that a lane stores 4 consecutive steps of one
+    // channel (16 bytes) and 32 lanes one row's 128 steps (whole lines): each wave writes
+    // and reads back only its own 16 x 128 block (rows 0..15, window columns tw..tw+127,
+    // inside a row of RS for an active wave); the main loop ended with a barrier, and a
+    // wave's LDS accesses complete in order. T_out is a multiple of 4, so the 4 steps are
+    // all in range or all out.
+    if (!active) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int nb = 0; nb < GN_NB; ++nb) zA[(4 * lq + r) * RS + tw + 16 * nb + l16] = y[nb][r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int item = l + 64 * i;
+      const int row = item >> 5, t = tw + 4 * (item & 31);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&zA[row * RS + t]);
+      if (t < a.T_out)
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<f32x4*>(outn + (size_t)(co0 + row) * a.T_out + t));
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* __restrict__ orow = outn + (size_t)(co0 + 4 * lq + r) * a.T_out;
+#pragma unroll
+      for (int nb = 0; nb < GN_NB; ++nb) {
+        const int t = tw + 16 * nb + l16;
+        if (valid[nb]) __builtin_nontemporal_store(y[nb][r], &orow[t]);
+      }
     }
   }
 }
