@@ -302,16 +302,54 @@ def test_groupnorm_unaligned_x():
     assert err <= TOL_F32, err
 
 
-def test_groupnorm_deterministic():
-    w = WORKLOADS[3].dims
-    announce("conv1d_groupnorm_fwd determinism", w)
-    q = to_dev(groupnorm_inputs(w["N"], w["C_in"], w["C_out"], w["T"], seed_for(3, 1)))
+@pytest.mark.parametrize("shape", [
+    (16, 128, 256, 1024, 32, 1, 1),   # the GN workload: single-launch path
+    (4, 64, 128, 2048, 16, 1, 1),     # T_out > 1024: two-launch path (tile partials)
+])
+def test_groupnorm_deterministic(shape):
+    """Bitwise-equal results over 10 calls in different launch orders: back to back, after
+    another kernel, on a second stream, and after a call of another shape (which leaves
+    other partials in the library's workspace on the two-launch path)."""
+    N, C_in, C_out, T, G, pad, dil = shape
+    announce("conv1d_groupnorm_fwd determinism", shape)
+    q = to_dev(groupnorm_inputs(N, C_in, C_out, T, 41))
+    o = to_dev(groupnorm_inputs(2, C_in, C_out, T // 2 + 3, 42))
+    blk = to_dev(prenorm_inputs(2, 64, 1000, 43))
+
+    def gn():
+        return dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"],
+                                       q["eps"], G, pad, dil)
+
+    side = torch.cuda.Stream()
     outs = []
-    for _ in range(5):
-        outs.append(dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"],
-                                            q["eps"], w["G"], w["padding"], w["dilation"]))
+    for i in range(10):
+        kind = i % 4
+        if kind == 1:
+            dc.prenorm_dconv1d_fwd(blk["x"], blk["running_mean"], blk["running_var"],
+                                   blk["gamma"], blk["beta"], blk["eps"], blk["W"], blk["b"], 7)
+        elif kind == 3:
+            dc.conv1d_groupnorm_fwd(o["x"], o["W"], o["bias"], o["gamma"], o["beta"], o["eps"],
+                                    G, pad, dil)
+        if kind == 2:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                outs.append(gn())
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            outs.append(gn())
     torch.cuda.synchronize()
-    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    assert all(torch.equal(outs[0], r) for r in outs[1:])
+
+
+def test_block_bf16_deterministic():
+    N, C, L, d = 2, 512, 1024, 128
+    announce("prenorm_dconv1d_fwd_bf16 determinism", (N, C, L, d))
+    q = to_dev(prenorm_inputs(N, C, L, 44, bf16=True))
+    outs = [dc.prenorm_dconv1d_fwd_bf16(q["x"], q["running_mean"], q["running_var"],
+                                        q["gamma"], q["beta"], q["eps"], q["W"], q["b"], d)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], r) for r in outs[1:])
 
 
 # ----------------------------------------------------------------- full benchmark workloads
