@@ -10,8 +10,12 @@ namespace dconv1d {
 // 16 output channels x T_out <= 1024 steps. The staged window is 64*mg steps wide
 // (gn_fused_groups; 0 when no instantiated width covers the shape) and starts at input
 // step -pad - delta; x is staged with 16-byte loads when gn_fused_vec4, and then delta
-// (gn_fused_delta) aligns the window start to a multiple of 4.
+// (gn_fused_delta) aligns the window start to a multiple of 4. gn_fused_groups returns
+// GN_PRIVATE instead when 128 + 2*dil + delta <= GN_PW: then each wave stages its own
+// GN_PW-step window, from step 128*wave - pad - delta on.
 constexpr int GN_MG_MAX = 19;
+constexpr int GN_PRIVATE = 1;   // mg value of the per-wave windows
+constexpr int GN_PW = 136;      // their width in steps (and LDS row pitch: 8 mod 16)
 struct GnFusedArgs {
   const float* x;       // [N][C_in][T]
   const float* W;       // [C_out][C_in][3], 8-byte aligned
@@ -23,7 +27,8 @@ struct GnFusedArgs {
   int N, C_in, C_out, T, T_out;
   int pad, dil;         // tap k reads input t - pad + k*dil
   int cpg;              // channels per group (divides 16)
-  int mg;               // staged window width in 64-step groups, gn_fused_groups(...)
+  int mg;               // staged window width in 64-step groups, or GN_PRIVATE
+                        // (gn_fused_groups(...))
   int vec4;             // 16-byte x loads, gn_fused_vec4(T, x)
   int delta;            // window start shift, gn_fused_delta(pad, vec4)
   int n_cb;             // C_out / 16

@@ -31,6 +31,16 @@
 //   LDS layout = row r (channel 16c + r) at r*RS floats, RS = 64*MG + 8: RS = 8 mod 16
 //                puts the rows 2lq of the four quarter-waves of a B read on different
 //                banks.
+//   private    = (MG = GN_PRIVATE, when 128 + 2*dil + delta <= GN_PW) every wave stages
+//   windows      all 16 rows of a chunk itself, over only the GN_PW input steps from
+//                128w - pad - delta on that its own 128 output steps read, into an LDS
+//                area of its own (row pitch GN_PW, also 8 mod 16). The neighbouring waves'
+//                windows overlap by 2*dil + delta steps (about 6% more L2 -> LDS traffic
+//                for dil = 1), and no wave reads another's area, so the chunk loop has no
+//                workgroup barrier: a wave's LDS accesses complete in program order, and
+//                the two waves of a SIMD drift apart, one in its MFMAs while the other
+//                loads and stages. The loads cover 16 rows x GN_PW steps with each lane's
+//                items spread over the rows; a row's items past T get the rejected offset.
 //   operands   = MFMA K-step (tap k, half g, e): quarter-wave lq = lane/16 supplies input
 //                channel 16c + 8g + 2lq + e. A = W[co0 + lane%16][16c + 8g + 2lq + e][k]:
 //                per half, six consecutive floats of the [C_out][C_in][3] layout per lane.
@@ -95,13 +105,15 @@ __device__ __forceinline__ double group_total(const float* red, int l, int cpg) 
 
 }  // namespace
 
-// MG: 64-step groups of the staged window (the window is 64*MG steps wide); VW: floats
-// per lane per load (1 or 4)
+// MG: 64-step groups of the shared staged window (the window is 64*MG steps wide), or
+// GN_PRIVATE for per-wave windows; VW: floats per lane per load (1 or 4)
 template <int MG, int VW>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * GN_WAVES, 64 * GN_WAVES)))
 conv_gn_fused_kernel(GnFusedArgs a) {
-  constexpr int RS = 64 * MG + 8;             // floats per staged row
-  constexpr int BUF = GN_CI * RS;             // floats per chunk buffer
+  // MG == GN_PRIVATE: each wave stages its own window (see the file comment)
+  constexpr bool PRIV = MG == GN_PRIVATE;
+  constexpr int RS = PRIV ? GN_PW : 64 * MG + 8;               // floats per staged row
+  constexpr int BUF = (PRIV ? GN_WAVES : 1) * GN_CI * RS;      // floats per chunk buffer
   __shared__ __attribute__((aligned(16))) float zA[BUF];
   __shared__ __attribute__((aligned(16))) float zB[BUF];
   __shared__ float red[GN_WAVES * 16];    // per (wave, row) partials: sums
@@ -123,7 +135,9 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   const int n = __builtin_amdgcn_readfirstlane(logical / a.n_cb);
   const int co0 = 16 * cb;
   const int tw = 128 * w;                 // first output step of this wave
-  const bool active = tw < a.T_out;       // waves past the end only stage
+  const bool active = tw < a.T_out;       // waves past the end only stage (shared window)
+  const int wz = PRIV ? w * GN_CI * RS : 0;   // this wave's LDS area (private windows)
+  const int tz = PRIV ? 0 : tw;               // LDS column of the wave's first output step
 
   const float* xn = a.x + (size_t)n * a.C_in * a.T;
   // this lane's weight row: W[co0 + l16][2lq][0] (see load_w)
@@ -142,45 +156,86 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   // into range).
   static_assert(VW == 1 || VW == 4, "4- or 16-byte loads");
   using XV = typename std::conditional<VW == 4, f32x4, float>::type;
-  constexpr int NL = (64 * MG + 64 * VW - 1) / (64 * VW);   // loads per row
-  const int ws = -a.pad - a.delta;
+  // Private windows: item i of the 16 x GN_PW window is row i / IPR, columns
+  // VW * (i % IPR) on, and lane l takes items l, l + 64, ... Shared window: loads per row.
+  constexpr int IPR = RS / VW;                                  // items per private row
+  constexpr int NL = PRIV ? (GN_CI * IPR + 63) / 64 : (64 * MG + 64 * VW - 1) / (64 * VW);
+  constexpr int NX = PRIV ? NL : 2 * NL;                        // loads per lane per chunk
+  const int ws = (PRIV ? tw : 0) - a.pad - a.delta;
   uint32_t voff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int j = 64 * VW * i + VW * l;
-    const int t = ws + j;
-    voff[i] = (t >= 0 && j < 64 * MG) ? 4u * (uint32_t)t : kOutOfRange;
+    if constexpr (PRIV) {
+      // byte offset within the chunk's 16 rows (one buffer range of 16*T floats), so
+      // steps past T are rejected here rather than by the range check
+      const int item = l + 64 * i, row = item / IPR, j = VW * (item % IPR);
+      const int t = ws + j;
+      voff[i] = (item < GN_CI * IPR && t >= 0 && t < a.T) ? 4u * (uint32_t)(row * a.T + t)
+                                                          : kOutOfRange;
+    } else {
+      const int j = 64 * VW * i + VW * l;
+      const int t = ws + j;
+      voff[i] = (t >= 0 && j < 64 * MG) ? 4u * (uint32_t)t : kOutOfRange;
+    }
     asm volatile("" : "+v"(voff[i]));
   }
-  // this wave's rows of chunk c (channels 16c + w and 16c + w + 8) into registers
-  XV xa[2][NL], xb[2][NL];
-  auto load_x = [&](int c, XV (&dst)[2][NL]) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo) -> XV {
+    if constexpr (VW == 4)
+      return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+    else
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo, 0, 0));
+  };
+  // This wave's part of chunk c into registers: the whole private window, or the shared
+  // window's rows 16c + w (dst[0 .. NL)) and 16c + w + 8 (dst[NL .. 2NL)).
+  XV xa[NX], xb[NX];
+  auto load_x = [&](int c, XV (&dst)[NX]) {
+    if constexpr (PRIV) {
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(xn + (size_t)(GN_CI * c + w + 8 * h) * a.T), (short)0, 4 * a.T,
+          const_cast<float*>(xn + (size_t)GN_CI * c * a.T), (short)0, 4 * GN_CI * a.T,
           kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        if constexpr (VW == 4)
-          dst[h][i] =
-              __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, 0));
-        else
-          dst[h][i] =
-              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], 0, 0));
+      for (int i = 0; i < NL; ++i) dst[i] = load_one(rs, voff[i]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(xn + (size_t)(GN_CI * c + w + 8 * h) * a.T), (short)0, 4 * a.T,
+            kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) dst[h * NL + i] = load_one(rs, voff[i]);
       }
     }
   };
-  // window columns past 64*MG (the tail of the last 16-byte load) are not stored
-  auto store_x = [&](const XV (&src)[2][NL], float* zb) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
+  // shared window: columns past 64*MG (the tail of the last 16-byte load) are not stored;
+  // private: items past the 16 rows are not stored
+  auto store_x = [&](const XV (&src)[NX], float* zb) {
+    if constexpr (PRIV) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int j = 64 * VW * i + VW * l;
-        if (64 * VW * (i + 1) <= 64 * MG || j < 64 * MG)
-          *reinterpret_cast<XV*>(zb + (w + 8 * h) * RS + j) = src[h][i];
+        const int item = l + 64 * i;
+        if (64 * (i + 1) <= GN_CI * IPR || item < GN_CI * IPR)
+          *reinterpret_cast<XV*>(zb + wz + (item / IPR) * RS + VW * (item % IPR)) = src[i];
       }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int j = 64 * VW * i + VW * l;
+          if (64 * VW * (i + 1) <= 64 * MG || j < 64 * MG)
+            *reinterpret_cast<XV*>(zb + (w + 8 * h) * RS + j) = src[h * NL + i];
+        }
+    }
+  };
+  // End of a chunk: the next chunk reads what this one staged. Shared window: every wave's
+  // rows, so a workgroup barrier. Private: only this wave's own area; the wave's LDS
+  // accesses complete in program order, so the fence only keeps the compiler from moving
+  // them across.
+  auto chunk_sync = [&] {
+    if constexpr (PRIV)
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    else
+      __syncthreads();
   };
   const int nC = a.C_in / GN_CI;
   // A operands of chunk c: W[co0 + l16][16c + 8g + 2lq + e][k] at wrow + 48c + 24g + 3e + k,
@@ -198,8 +253,8 @@ conv_gn_fused_kernel(GnFusedArgs a) {
       }
     }
   };
-  // B operand base of this lane: row 2lq, window column tw + l16 + delta
-  const int boff = 2 * lq * RS + tw + l16 + a.delta;
+  // B operand base of this lane: row 2lq, window column tz + l16 + delta
+  const int boff = wz + 2 * lq * RS + tz + l16 + a.delta;
   // the chunk's 96 MFMAs of this wave on buffer zb, in six steps (tap k, half g); the B
   // operands of the next step are read while the current step's MFMAs run
   auto compute = [&](const float* zb, const float (&wv)[12]) {
@@ -229,31 +284,34 @@ conv_gn_fused_kernel(GnFusedArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // one chunk: the weights of chunk c + 1 and the x row of chunk c + 2 go out, chunk c
-  // computes from buffer zc, then chunk c + 1's row (loaded a chunk ago) goes to buffer zn
-  // (last read by chunk c - 1, which every wave finished before the previous barrier)
+  // one chunk: the weights of chunk c + 1 and the x of chunk c + 2 go out, chunk c
+  // computes from buffer zc, then chunk c + 1's x (loaded a chunk ago) goes to buffer zn
+  // (last read by chunk c - 1, finished before the previous chunk_sync)
   auto chunk = [&](int c, const float* zc, float* zn, const float (&wc)[12], float (&w1)[12],
-                   XV (&x2)[2][NL], const XV (&x1)[2][NL]) {
+                   XV (&x2)[NX], const XV (&x1)[NX]) {
     load_w(c + 1, w1);
     load_x(min(c + 2, nC - 1), x2);
     __builtin_amdgcn_sched_barrier(0);
     compute(zc, wc);
     if (c + 1 < nC) store_x(x1, zn);
-    __syncthreads();
+    chunk_sync();
   };
 
-  float wA[12], wB[12];
-  load_w(0, wA);
-  load_x(0, xa);
-  load_x(min(1, nC - 1), xb);
-  store_x(xa, zA);
-  __syncthreads();
-  int c = 0;
-  for (; c + 1 < nC; c += 2) {
-    chunk(c, zA, zB, wA, wB, xa, xb);
-    chunk(c + 1, zB, zA, wB, wA, xb, xa);
+  // private windows: a wave past the end has nothing to stage for anyone
+  if (!PRIV || active) {
+    float wA[12], wB[12];
+    load_w(0, wA);
+    load_x(0, xa);
+    load_x(min(1, nC - 1), xb);
+    store_x(xa, zA);
+    chunk_sync();
+    int c = 0;
+    for (; c + 1 < nC; c += 2) {
+      chunk(c, zA, zB, wA, wB, xa, xb);
+      chunk(c + 1, zB, zA, wB, wA, xb, xa);
+    }
+    if (c < nC) chunk(c, zA, zB, wA, wB, xa, xb);
   }
-  if (c < nC) chunk(c, zA, zB, wA, wB, xa, xb);
 
   // Epilogue. Register r of block nb holds channel co0 + 4lq + r, step tw + 16nb + l16.
   const int cpg = a.cpg;
@@ -321,20 +379,21 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   if (vec_out) {
     // Through the idle staging buffer zA, so that a lane stores 4 consecutive steps of one
     // channel (16 bytes) and 32 lanes one row's 128 steps (whole lines): each wave writes
-    // and reads back only its own 16 x 128 block (rows 0..15, window columns tw..tw+127,
-    // inside a row of RS for an active wave); the main loop ended with a barrier, and a
-    // wave's LDS accesses complete in order. T_out is a multiple of 4, so the 4 steps are
-    // all in range or all out.
+    // and reads back only its own 16 x 128 block (rows 0..15 of its area, columns
+    // tz..tz+127, inside a row of RS for an active wave); the statistics passes ended with
+    // barriers, and a wave's LDS accesses complete in order. T_out is a multiple of 4, so
+    // the 4 steps are all in range or all out.
     if (!active) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int nb = 0; nb < GN_NB; ++nb) zA[(4 * lq + r) * RS + tw + 16 * nb + l16] = y[nb][r];
+      for (int nb = 0; nb < GN_NB; ++nb)
+        zA[wz + (4 * lq + r) * RS + tz + 16 * nb + l16] = y[nb][r];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int item = l + 64 * i;
-      const int row = item >> 5, t = tw + 4 * (item & 31);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&zA[row * RS + t]);
+      const int row = item >> 5, j = 4 * (item & 31), t = tw + j;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&zA[wz + row * RS + tz + j]);
       if (t < a.T_out)
         __builtin_nontemporal_store(
             v, reinterpret_cast<f32x4*>(outn + (size_t)(co0 + row) * a.T_out + t));
@@ -353,6 +412,7 @@ conv_gn_fused_kernel(GnFusedArgs a) {
 }
 
 int gn_fused_groups(int T_out, int dil, int delta) {
+  if (128LL + 2LL * dil + delta <= GN_PW) return GN_PRIVATE;
   const long long span = 128LL * ((T_out + 127) / 128) + 2LL * dil + delta;
   const int need = (int)((span + 63) / 64);
   for (int mg : {4, 8, 12, 17, 19})
@@ -377,6 +437,9 @@ bool gn_fused_fits(long long N, int C_in, int C_out, int T, int T_out, int pad, 
 template <int VW>
 static void launch_mg(const GnFusedArgs& a, int mg, dim3 grid, dim3 block, hipStream_t stream) {
   switch (mg) {
+    case GN_PRIVATE:
+      hipLaunchKernelGGL((conv_gn_fused_kernel<GN_PRIVATE, VW>), grid, block, 0, stream, a);
+      break;
     case 4: hipLaunchKernelGGL((conv_gn_fused_kernel<4, VW>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((conv_gn_fused_kernel<8, VW>), grid, block, 0, stream, a); break;
     case 12: hipLaunchKernelGGL((conv_gn_fused_kernel<12, VW>), grid, block, 0, stream, a); break;

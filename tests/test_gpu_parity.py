@@ -247,6 +247,17 @@ GN_CASES = [
     (3, 64, 256, 1024, 32, 1, 1, True, True),    # the GN workload's layer with a bias
     (2, 32, 64, 512, 8, 2, 2, False, True),      # window shift 2 (16-byte loads)
     (40, 32, 128, 256, 16, 1, 1, True, True),    # 320 workgroups: more than one per CU
+    # of the single-launch cases above, those with 128 + 2*dil + delta <= 136 (delta: 0..3
+    # with 16-byte loads, 0 with 4-byte ones) stage per-wave windows; the rest (taps 200
+    # or 256 apart, pad 96 or 97) and these share one window per workgroup:
+    (2, 16, 32, 301, 4, 5, 5, True, True),       # shared window, 4-byte loads, 3 waves
+    (2, 32, 64, 400, 8, 5, 5, False, True),      # shared window, 16-byte loads, delta 3
+    # per-wave windows at their edges
+    (2, 32, 64, 777, 8, 1, 1, True, True),       # 4-byte loads, 7 waves, ragged last wave
+    (2, 16, 32, 1004, 4, 3, 3, False, True),     # 16-byte loads, 128 + 6 + 1 = 135 steps
+    (2, 16, 32, 1006, 4, 4, 4, False, True),     # 4-byte loads, 128 + 8 = 136: widest
+    (2, 16, 32, 1008, 4, 0, 1, True, True),      # pad 0: delta 0, T_out = 1006
+    (1, 48, 16, 130, 16, 2, 1, True, True),      # two waves, the second with 4 steps
 ]
 
 
