@@ -32,6 +32,18 @@ for _ in range(12):
                       G * int(RNG.integers(1, 40)), int(RNG.integers(8, 600)), G,
                       int(RNG.integers(0, 4)), int(RNG.integers(1, 4)), bool(RNG.integers(0, 2))))
 
+# shapes the single-launch GN kernel takes (C_in and C_out multiples of 16, channels per
+# group dividing 16, T_out <= 1024) or just misses (T_out up to 1100): per-wave windows for
+# small dil and pad, one shared window otherwise, the two-launch path past 1024 steps
+RNG_GN1 = np.random.default_rng(20261203)
+GN1_SHAPES = []
+for _ in range(12):
+    cpg = int(RNG_GN1.choice([1, 2, 4, 8, 16]))
+    C_out = 16 * int(RNG_GN1.integers(1, 9))
+    GN1_SHAPES.append((int(RNG_GN1.integers(1, 4)), 16 * int(RNG_GN1.integers(1, 9)), C_out,
+                       int(RNG_GN1.integers(8, 1100)), C_out // cpg, int(RNG_GN1.integers(0, 6)),
+                       int(RNG_GN1.integers(1, 7)), bool(RNG_GN1.integers(0, 2))))
+
 
 @pytest.mark.parametrize("N,C,L,d", BLOCK_SHAPES)
 @pytest.mark.parametrize("mode", ["eval", "eval_bf16", "train", "external"])
@@ -78,7 +90,7 @@ def test_random_wide_bf16_block(N, C, L, d):
     assert err <= TOL_BF16, err
 
 
-@pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil,bias", GN_SHAPES)
+@pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil,bias", GN_SHAPES + GN1_SHAPES)
 def test_random_groupnorm(N, C_in, C_out, T, G, pad, dil, bias):
     if T + 2 * pad - 2 * dil < 1:
         pytest.skip("empty output")
