@@ -165,8 +165,10 @@ conv_bf16_kernel(ConvF32Args a) {
     const int c = q / 3, k = q - 3 * c;
     const int off = k * a.dil - a.pad;
     if (PAIR) {
-      const int ts = t0 + 2 * l + off;
-      const int vo = 2 * min(max(ts, 0), a.L_in - 2);
+      // a padded tap may read any in-range pair: store_z masks it to zero (with even
+      // offsets and even L an in-range pair start is at most L_in - 2)
+      const uint32_t ts = tap_step(t0 + 2 * l, off);
+      const int vo = 2 * (ts < (uint32_t)a.L_in ? (int)ts : 0);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
@@ -175,8 +177,8 @@ conv_bf16_kernel(ConvF32Args a) {
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int ts = t0 + l + 64 * j + off;
-        const int vo = 2 * min(max(ts, 0), a.L_in - 1);
+        const uint32_t ts = tap_step(t0 + l + 64 * j, off);
+        const int vo = 2 * (ts < (uint32_t)a.L_in ? (int)ts : 0);
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
           const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
@@ -190,8 +192,8 @@ conv_bf16_kernel(ConvF32Args a) {
   // steps per load (64 lanes x 4 bytes), straight into LDS.
   auto dma_x0 = [&](int q, int i0 = 0, int cnt = KCB / WV) {
     const int c = q / 3, k = q - 3 * c;
-    const int ts = t0 + 2 * l + k * a.dil - a.pad;
-    const int vo = 2 * min(max(ts, 0), a.L_in - 2);
+    const uint32_t ts = tap_step(t0 + 2 * l, k * a.dil - a.pad);
+    const int vo = 2 * (ts < (uint32_t)a.L_in ? (int)ts : 0);
 #pragma unroll
     for (int i = i0; i < i0 + cnt; ++i) {
       const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
@@ -202,8 +204,8 @@ conv_bf16_kernel(ConvF32Args a) {
   };
   auto dma_x1 = [&](int q, int i0 = 0, int cnt = KCB / WV) {
     const int c = q / 3, k = q - 3 * c;
-    const int ts = t0 + 2 * l + k * a.dil - a.pad;
-    const int vo = 2 * min(max(ts, 0), a.L_in - 2);
+    const uint32_t ts = tap_step(t0 + 2 * l, k * a.dil - a.pad);
+    const int vo = 2 * (ts < (uint32_t)a.L_in ? (int)ts : 0);
 #pragma unroll
     for (int i = i0; i < i0 + cnt; ++i) {
       const int ci = min(c * KCB + RPW * w + i, a.C_in - 1);
@@ -248,9 +250,8 @@ conv_bf16_kernel(ConvF32Args a) {
     const int c = q / 3, k = q - 3 * c;
     const int off = k * a.dil - a.pad;
     if (PAIR) {
-      const int ts = t0 + 2 * l + off;
       // with even offsets and even L both time steps of the pair are in or out together
-      uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
+      uint32_t tkeep = tap_step(t0 + 2 * l, off) < (uint32_t)a.L_in ? 0xffffffffu : 0u;
       asm volatile("" : "+v"(tkeep));
       stage_column([&](int i) { return bf16_lo(xr[i]); }, 2 * l, tkeep, dst);
       stage_column([&](int i) { return bf16_hi(xr[i]); }, 2 * l + 1, tkeep, dst);
@@ -258,8 +259,7 @@ conv_bf16_kernel(ConvF32Args a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = l + 64 * j;
-        const int ts = t0 + col + off;
-        uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
+        uint32_t tkeep = tap_step(t0 + col, off) < (uint32_t)a.L_in ? 0xffffffffu : 0u;
         asm volatile("" : "+v"(tkeep));
         stage_column([&](int i) { return bf16_to_f32((uint16_t)xr[j * RPW + i]); }, col, tkeep,
                      dst);

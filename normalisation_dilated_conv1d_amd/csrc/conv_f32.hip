@@ -118,10 +118,12 @@ conv_f32_kernel(ConvF32Args a) {
 
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
+    const int off = k * a.dil - a.pad;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int ts = t0 + l + 64 * j + k * a.dil - a.pad;
-      const int tsc = min(max(ts, 0), a.L_in - 1);
+      // a padded tap may read any in-range step: store_z masks it to zero
+      const uint32_t ts = tap_step(t0 + l + 64 * j, off);
+      const int tsc = ts < (uint32_t)a.L_in ? (int)ts : 0;
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int ci = min(c * KC + RPW * w + i, a.C_in - 1);
@@ -138,11 +140,11 @@ conv_f32_kernel(ConvF32Args a) {
   };
   auto store_z = [&](int q, float* dst) {
     const int c = q / 3, k = q - 3 * c;
+    const int off = k * a.dil - a.pad;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int col = l + 64 * j;
-      const int ts = t0 + col + k * a.dil - a.pad;
-      uint32_t tkeep = (ts >= 0 && ts < a.L_in) ? 0xffffffffu : 0u;
+      uint32_t tkeep = tap_step(t0 + col, off) < (uint32_t)a.L_in ? 0xffffffffu : 0u;
       asm volatile("" : "+v"(tkeep));
       const int pos = 64 * j + (col & 15) * 4 + ((col & 63) >> 4);
 #pragma unroll

@@ -37,6 +37,15 @@ enum ConvEpilogue { EPI_RESIDUAL = 0, EPI_GN_STATS = 1 };
 
 inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
 
+// Input step read by output step `s` (a tile start plus a column: below L_in + 2^10) at
+// tap offset `off` = k*dil - pad (in [-L_in, L_in] for the block, whose padding is its
+// dilation clamped to L_in). The sum is formed in unsigned arithmetic, whose wrap-around
+// is defined, so it cannot overflow int when L_in is near 2^30; the result is below
+// L_in exactly when the tap lies inside the input.
+__device__ __forceinline__ uint32_t tap_step(int s, int off) {
+  return (uint32_t)s + (uint32_t)off;
+}
+
 // prep.hip
 hipError_t launch_prep_f32(const float* W, int C_out, int C_in, int Cout_pad, int Cin_pad,
                            float* Wp, const float* running_mean, const float* running_var,

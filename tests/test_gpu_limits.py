@@ -72,6 +72,38 @@ def test_block_largest_sample(bf16, L, d):
     assert err <= (TOL_BF16 if bf16 else TOL_F32), err
 
 
+@pytest.mark.parametrize("bf16,L,d", [(False, 2 ** 30 - 1, 2 ** 30 - 4),
+                                       (False, 2 ** 30 - 1, 2 ** 30 + 5),
+                                       (True, 2 ** 30 - 2, 2 ** 30 - 6)],
+                         ids=["f32_d_below_L", "f32_d_above_L", "bf16_d_below_L"])
+def test_block_longest_length(bf16, L, d):
+    """C = 1 at the longest length the ABI takes (L < 2^30). Tile start + column + tap
+    offset then reaches about 2L = 2^31, past the int range, so this checks that the tap
+    index is formed without overflow; with d just below L both padded and in-range outer
+    taps occur at each end of the sequence (d >= L leaves the centre tap only)."""
+    C = 1
+    announce("longest length", "bf16" if bf16 else "f32", (1, C, L, d))
+    p = _device_block_inputs(C, L, 70_400 + bf16 + (d > L), bf16)
+    fn = dc.prenorm_dconv1d_fwd_bf16 if bf16 else dc.prenorm_dconv1d_fwd
+    out = fn(p["x"], p["running_mean"], p["running_var"], p["gamma"], p["beta"], p["eps"],
+             p["W"], p["b"], d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    de = min(d, L)
+    ts = sorted({0, 1, 2, 3, 4, 5, 127, 128, L // 2, L - de - 1, L - de, L - de + 1,
+                 de - 1, de, de + 1, L - 129, L - 128, L - 6, L - 5, L - 4, L - 3, L - 2,
+                 L - 1} & set(range(L)))
+    pts = [(0, 0, t) for t in ts] + [(0, 0, int(rng.integers(L))) for _ in range(40)]
+    ref = oracle.prenorm_block_points(p["x"], p["running_mean"], p["running_var"], p["gamma"],
+                                      p["beta"], p["eps"], p["W"], p["b"], d, pts)
+    got = np.array([float(out[n, c, t].float()) for (n, c, t) in pts])
+    del out, p
+    torch.cuda.empty_cache()
+    dc.release()
+    err = maxrel(got, ref)
+    assert err <= (TOL_BF16 if bf16 else TOL_F32), err
+
+
 def test_block_many_tiny_samples():
     """N = 20000 samples of (3, 5): one workgroup per sample, mostly padding."""
     N, C, L, d = 20000, 3, 5, 2
