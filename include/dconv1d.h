@@ -33,8 +33,13 @@
  *     GroupNorm partial statistics). It is allocated with hipMalloc on the first call
  *     that needs more than the current size (hipFree of the old one synchronises the
  *     device), kept for later calls, and freed by dconv1d_release().
- *   - All calls on one device share that workspace: calls that may overlap in time
- *     on different streams of the same device race. Serialise them on one stream.
+ *   - All calls on one device share that workspace, and the library orders them: a
+ *     call whose stream differs from that of the workspace's previous user makes its
+ *     stream wait (on the device, through an event; the host does not block) for that
+ *     call's kernels. Calls queued under stream capture skip this ordering (an event
+ *     may not be waited on across the capture boundary); a captured call and calls on
+ *     other streams must then be ordered by the caller. The single-launch GroupNorm
+ *     path uses no workspace and needs no ordering.
  *   - No host synchronisation and no device-to-host reads happen on a call once the
  *     workspace is large enough; the call returns as soon as its kernels are queued.
  *   - Argument validation happens on the host before any HIP call; a rejected call

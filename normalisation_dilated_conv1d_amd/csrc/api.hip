@@ -44,45 +44,104 @@ bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
 }
 
 // ---------------------------------------------------------------- per-device workspace
+// One workspace per device holds what a call's kernels share (folded BN vectors,
+// repacked weights, partial statistics). Calls on different streams of one device would
+// race on it, so every call that uses it holds the device's lock while it queues its
+// kernels, waits (on the device, through an event, without blocking the host) for the
+// last call that used it when that call ran on another stream, and records the event
+// after its own last kernel.
 constexpr int kMaxDevices = 64;
 struct Workspace {
+  std::mutex mu;
   void* ptr = nullptr;
   size_t bytes = 0;
+  hipEvent_t done = nullptr;   // recorded after the last call's last kernel
+  hipStream_t last = nullptr;  // the stream that call ran on
+  bool pending = false;        // `done` has been recorded
 };
-std::mutex g_ws_mu;
 Workspace g_ws[kMaxDevices];
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-int get_workspace(size_t bytes, char** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(DCONV1D_EINVAL, "device %d out of range", dev);
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  Workspace& w = g_ws[dev];
-  if (w.bytes < bytes) {
-    if (w.ptr) {
-      // earlier calls may still be using the old buffer
-      e = hipDeviceSynchronize();
-      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-      (void)hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    const size_t sz = (bytes + (size_t(2) << 20) - 1) & ~((size_t(2) << 20) - 1);
-    e = hipMalloc(&w.ptr, sz);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      w.ptr = nullptr;
-      return fail(DCONV1D_ENOMEM, "workspace hipMalloc of %zu bytes failed: %s", sz,
-                  hipGetErrorString(e));
-    }
-    w.bytes = sz;
-  }
-  *out = static_cast<char*>(w.ptr);
-  return DCONV1D_OK;
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
 }
+
+// Holds a device's workspace for the duration of one call.
+class WorkspaceUse {
+ public:
+  // Locks the current device's workspace, grows it to at least `bytes` and orders
+  // `stream` after the previous user of the workspace. On success *out is the
+  // workspace. Under stream capture the event ordering is skipped (an event recorded or
+  // waited on across the capture boundary is not allowed): captured calls are ordered
+  // against other streams by the caller.
+  int acquire(size_t bytes, hipStream_t stream, char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DCONV1D_EINVAL, "device %d out of range", dev);
+    w_ = &g_ws[dev];
+    lock_ = std::unique_lock<std::mutex>(w_->mu);
+    stream_ = stream;
+    captured_ = capturing(stream);
+    if (w_->bytes < bytes) {
+      if (w_->ptr) {
+        // earlier calls may still be using the old buffer
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        (void)hipFree(w_->ptr);
+        w_->ptr = nullptr;
+        w_->bytes = 0;
+      }
+      const size_t sz = (bytes + (size_t(2) << 20) - 1) & ~((size_t(2) << 20) - 1);
+      e = hipMalloc(&w_->ptr, sz);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        w_->ptr = nullptr;
+        return fail(DCONV1D_ENOMEM, "workspace hipMalloc of %zu bytes failed: %s", sz,
+                    hipGetErrorString(e));
+      }
+      w_->bytes = sz;
+    }
+    if (!captured_) {
+      if (!w_->done) {
+        e = hipEventCreateWithFlags(&w_->done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+          w_->done = nullptr;
+          return hip_fail(e, "hipEventCreateWithFlags");
+        }
+      }
+      if (w_->pending && w_->last != stream) {
+        e = hipStreamWaitEvent(stream, w_->done, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+      }
+    }
+    held_ = true;
+    *out = static_cast<char*>(w_->ptr);
+    return DCONV1D_OK;
+  }
+  // Marks the end of this call's use (after its last kernel is queued, or after a failed
+  // launch: whatever was queued still uses the workspace).
+  ~WorkspaceUse() {
+    if (!held_ || captured_) return;
+    if (hipEventRecord(w_->done, stream_) == hipSuccess) {
+      w_->last = stream_;
+      w_->pending = true;
+    } else {
+      // without the event later calls cannot be ordered after this one: wait here
+      (void)hipStreamSynchronize(stream_);
+      w_->pending = false;
+    }
+  }
+
+ private:
+  Workspace* w_ = nullptr;
+  std::unique_lock<std::mutex> lock_;
+  hipStream_t stream_ = nullptr;
+  bool captured_ = false;
+  bool held_ = false;
+};
 
 // ---------------------------------------------------------------- kernel timer
 constexpr int kTimerSlots = 4096;
@@ -227,7 +286,8 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   const size_t part_bytes = train ? bn_train_partials_bytes((int)N, Ci, Li) : 0;
   const size_t total = align256(off_part + part_bytes);
   char* ws = nullptr;
-  st = get_workspace(total, &ws);
+  WorkspaceUse use;
+  st = use.acquire(total, stream, &ws);
   if (st != DCONV1D_OK) return st;
   float* scale = reinterpret_cast<float*>(ws + off_scale);
   float* shift = reinterpret_cast<float*>(ws + off_shift);
@@ -414,7 +474,8 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
   const size_t off_part = align256(off_wp + sizeof(float) * 3 * (size_t)Cin_pad * Cout_pad);
   const size_t total = align256(off_part + sizeof(float) * 2 * (size_t)N * C_out * n_tt);
   char* ws = nullptr;
-  int st = get_workspace(total, &ws);
+  WorkspaceUse use;
+  int st = use.acquire(total, stream, &ws);
   if (st != DCONV1D_OK) return st;
   float* Wp = reinterpret_cast<float*>(ws + off_wp);
   float* part = reinterpret_cast<float*>(ws + off_part);
@@ -456,17 +517,22 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
 const char* dconv1d_last_error(void) { return g_err.c_str(); }
 
 void dconv1d_release(void) {
-  std::lock_guard<std::mutex> lock(g_ws_mu);
   int cur = 0;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (int dev = 0; dev < kMaxDevices; ++dev) {
-    if (!g_ws[dev].ptr) continue;
+    Workspace& w = g_ws[dev];
+    std::lock_guard<std::mutex> lock(w.mu);
+    if (!w.ptr && !w.done) continue;
     if (hipSetDevice(dev) == hipSuccess) {
       (void)hipDeviceSynchronize();
-      (void)hipFree(g_ws[dev].ptr);
+      if (w.ptr) (void)hipFree(w.ptr);
+      if (w.done) (void)hipEventDestroy(w.done);
     }
-    g_ws[dev].ptr = nullptr;
-    g_ws[dev].bytes = 0;
+    w.ptr = nullptr;
+    w.bytes = 0;
+    w.done = nullptr;
+    w.last = nullptr;
+    w.pending = false;
   }
   if (have_cur) (void)hipSetDevice(cur);
 }
