@@ -218,9 +218,10 @@ def group_norm(y, num_groups: int, gamma, beta, eps):
 
     For each (n, g): mean and biased variance (divide by the element count) over the
     group's channels and all time steps, both taken two-pass in float64; then
-    (y - mean)/sqrt(var + eps), then gamma[c]*. + beta[c] when the affine parameters
-    are given (FW-GLM-5-1__l2_p35, GroupNorm definition and its normalise kernel,
-    which skips the affine step when gamma is absent).
+    (y - mean)/sqrt(var + eps), then gamma[c]*. + beta[c] (FW-GLM-5-1__l2_p35,
+    GroupNorm definition and its normalise kernel). That kernel applies gamma and beta
+    together, or neither when gamma is absent; each may be None here on its own, meaning
+    gamma = 1 or beta = 0 (PyTorch's group_norm convention, an extension of the page).
     """
     y = _f64(y)
     N, C, T = y.shape

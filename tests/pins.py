@@ -466,5 +466,23 @@ def gn_scale_invariance(fn):
     return err <= 1e-12, f"scale invariance err {err:.3g}"
 
 
+def gn_partial_affine_torch(fn):
+    """gamma or beta absent on its own (None means gamma = 1 or beta = 0): torch float64
+    group_norm with weight=None or bias=None, and the affine-free result scaled or shifted
+    by hand (so a dropped or doubled beta, or a gamma applied to beta, fails)."""
+    worst = 0.0
+    for seed, drop in ((51, "gamma"), (52, "beta")):
+        p = _rand_gn(2, 6, 12, 40, seed, bias=True)
+        p[drop] = None
+        worst = max(worst, _maxrel(_call_gn(fn, p, 4), _torch_gn(p, 4)))
+        plain = _call_gn(fn, dict(p, gamma=None, beta=None), 4)
+        if drop == "gamma":
+            exp = plain + p["beta"][None, :, None]
+        else:
+            exp = plain * p["gamma"][None, :, None]
+        worst = max(worst, _maxrel(_call_gn(fn, p, 4), exp))
+    return worst <= 1e-12, f"partial affine max rel err {worst:.3g}"
+
+
 GN_PINS = [gn_hand_golden, gn_brute_tiny, gn_torch_f64, gn_instance_and_layer_norm,
-           gn_moments, gn_scale_invariance]
+           gn_moments, gn_scale_invariance, gn_partial_affine_torch]

@@ -93,7 +93,15 @@ def _g_stats_per_channel(x, W, bias, gamma, beta, eps, G, padding=1, dilation=1)
     return oracle.conv_groupnorm(x, W, bias, gamma, beta, eps, C, padding, dilation)
 
 
-GN_MUTANTS = [_g_unbiased, _g_interleaved_groups, _g_no_beta, _g_no_padding, _g_stats_per_channel]
+def _g_beta_needs_gamma(x, W, bias, gamma, beta, eps, G, padding=1, dilation=1):
+    # beta skipped whenever gamma is absent (the affine step only with gamma present)
+    if gamma is None:
+        beta = None
+    return oracle.conv_groupnorm(x, W, bias, gamma, beta, eps, G, padding, dilation)
+
+
+GN_MUTANTS = [_g_unbiased, _g_interleaved_groups, _g_no_beta, _g_no_padding, _g_stats_per_channel,
+              _g_beta_needs_gamma]
 
 
 def _t_unbiased_norm(x, rm, rv, g, b_, eps, mom, W, b, d):
