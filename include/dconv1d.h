@@ -98,6 +98,30 @@ int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* 
                         int64_t N, int64_t C, int64_t L, int64_t d, hipStream_t stream);
 
 /*
+ * prenorm_dconv1d_fwd_noalloc - prenorm_dconv1d_fwd that allocates nothing, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Arguments, layout, arithmetic and results are those of prenorm_dconv1d_fwd (the same
+ * kernels run). Limit: C <= 512 (DCONV1D_NOALLOC_MAX_C); larger C gives DCONV1D_EINVAL
+ * with nothing queued. Instead of the workspace, the folded BN vectors and the
+ * repacked weights go to a fixed device array inside the library (3 MiB + 4 KiB per
+ * device, held until the process ends). No call allocates or frees device memory; the
+ * first call on a device looks up that device's copy of the array once. Every call on
+ * a device shares its array and overwrites what the previous call left there (nothing
+ * in it needs clearing: each call writes all of it it reads). Calls that may overlap
+ * in time on one device (different streams, or a replayed graph beside another call)
+ * race on the array and give wrong results: the caller must order them. Calls of the
+ * other entry points do not touch the array.
+ */
+#define DCONV1D_NOALLOC_MAX_C 512
+int prenorm_dconv1d_fwd_noalloc(const float* x, const float* running_mean,
+                                const float* running_var, const float* gamma,
+                                const float* beta, float eps, const float* W, const float* b,
+                                float* out, int64_t N, int64_t C, int64_t L, int64_t d,
+                                hipStream_t stream);
+
+/*
  * prenorm_dconv1d_fwd_bf16 - the same block with bfloat16 storage of x and out.
  *
  * x and out are bfloat16 bit patterns (uint16_t, [N][C][L]); every other argument is

@@ -46,6 +46,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, F, I64, S = ctypes.c_void_p, ctypes.c_float, ctypes.c_int64, ctypes.c_void_p
     lib.prenorm_dconv1d_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I64, I64, I64, I64, S]
     lib.prenorm_dconv1d_fwd.restype = ctypes.c_int
+    lib.prenorm_dconv1d_fwd_noalloc.argtypes = [P, P, P, P, P, F, P, P, P, I64, I64, I64, I64, S]
+    lib.prenorm_dconv1d_fwd_noalloc.restype = ctypes.c_int
     lib.prenorm_dconv1d_fwd_bf16.argtypes = [P, P, P, P, P, F, P, P, P, I64, I64, I64, I64, S]
     lib.prenorm_dconv1d_fwd_bf16.restype = ctypes.c_int
     train_args = [P, P, P, P, P, F, F, P, P, P, P, P, I64, I64, I64, I64, S]
@@ -142,6 +144,15 @@ def prenorm_dconv1d_fwd(x, running_mean, running_var, gamma, beta, eps, W, b, d,
     Runs on torch's current stream of x's device; returns ``out`` (allocated if None)."""
     return _prenorm("prenorm_dconv1d_fwd", x, running_mean, running_var, gamma, beta, eps, W,
                     b, d, out, torch.float32)
+
+
+def prenorm_dconv1d_fwd_noalloc(x, running_mean, running_var, gamma, beta, eps, W, b, d,
+                                out=None):
+    """prenorm_dconv1d_fwd through the entry point that allocates no device memory (its
+    scratch is a fixed array inside the library; C <= 512). Pass ``out`` to keep the call
+    free of allocations on the torch side too."""
+    return _prenorm("prenorm_dconv1d_fwd_noalloc", x, running_mean, running_var, gamma, beta,
+                    eps, W, b, d, out, torch.float32)
 
 
 def prenorm_dconv1d_fwd_bf16(x, running_mean, running_var, gamma, beta, eps, W, b, d, out=None):

@@ -143,6 +143,40 @@ class WorkspaceUse {
   bool held_ = false;
 };
 
+// ---------------------------------------------------------------- fixed scratch array
+// prenorm_dconv1d_fwd_noalloc keeps its folded BN vectors and repacked weights in this
+// fixed device array instead of the workspace, so that it never allocates. It is sized
+// for the float32 layout prenorm_common uses (scale, shift, repacked W, each 256-byte
+// aligned) at C = kNoallocMaxC: 2 KiB + 2 KiB + 3 MiB. Every device the library runs on
+// holds its own copy until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: the device address comes from hipGetSymbolAddress, looked
+// up once per device (with that device current) and kept in g_scratch_ptr.
+constexpr int64_t kNoallocMaxC = 512;
+constexpr size_t kScratchBytes = 2 * (4 * kNoallocMaxC) + 3 * 4 * size_t(kNoallocMaxC) * kNoallocMaxC;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DCONV1D_EINVAL, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "hipGetSymbolAddress of the scratch array");
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return DCONV1D_OK;
+}
+
 // ---------------------------------------------------------------- kernel timer
 constexpr int kTimerSlots = 4096;
 struct Timer {
@@ -205,7 +239,8 @@ template <typename XT>
 int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
                    const float* running_var, const float* gamma, const float* beta, float eps,
                    const float* W, const float* b, XT* out, int64_t N, int64_t C, int64_t L,
-                   int64_t d, hipStream_t stream, bool bf16, Norm norm, const TrainBn* train) {
+                   int64_t d, hipStream_t stream, bool bf16, Norm norm, const TrainBn* train,
+                   bool fixed_scratch = false) {
   // an empty batch has no data: x and out may then be NULL (torch gives empty tensors
   // a null data pointer)
   if (!x && N != 0) return fail(DCONV1D_EINVAL, "x is NULL");
@@ -227,6 +262,10 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   if (!out && N != 0) return fail(DCONV1D_EINVAL, "out is NULL");
   int st = check_sizes_block(N, C, L, d, eps);
   if (st != DCONV1D_OK) return st;
+  if (fixed_scratch && C > kNoallocMaxC)
+    return fail(DCONV1D_EINVAL, "C = %lld exceeds the %lld channels the no-allocation "
+                "entry point's fixed scratch array holds", (long long)C,
+                (long long)kNoallocMaxC);
   const int64_t per_sample = C * L;
   if (N > INT64_MAX / (per_sample * (int64_t)sizeof(XT)))
     return fail(DCONV1D_EINVAL, "N*C*L overflows");
@@ -287,7 +326,14 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   const size_t total = align256(off_part + part_bytes);
   char* ws = nullptr;
   WorkspaceUse use;
-  st = use.acquire(total, stream, &ws);
+  if (fixed_scratch) {
+    if (total > kScratchBytes)   // not reached: C <= kNoallocMaxC fits by construction
+      return fail(DCONV1D_EINVAL, "scratch of %zu bytes needed, %zu available", total,
+                  kScratchBytes);
+    st = scratch_address(&ws);
+  } else {
+    st = use.acquire(total, stream, &ws);
+  }
   if (st != DCONV1D_OK) return st;
   float* scale = reinterpret_cast<float*>(ws + off_scale);
   float* shift = reinterpret_cast<float*>(ws + off_shift);
@@ -350,6 +396,15 @@ int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* 
   g_err.clear();
   return prenorm_common<float>(x, x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
                                C, L, d, stream, false, Norm::Eval, nullptr);
+}
+
+int prenorm_dconv1d_fwd_noalloc(const float* x, const float* running_mean,
+                                const float* running_var, const float* gamma, const float* beta,
+                                float eps, const float* W, const float* b, float* out, int64_t N,
+                                int64_t C, int64_t L, int64_t d, hipStream_t stream) {
+  g_err.clear();
+  return prenorm_common<float>(x, x, running_mean, running_var, gamma, beta, eps, W, b, out, N,
+                               C, L, d, stream, false, Norm::Eval, nullptr, true);
 }
 
 int prenorm_dconv1d_fwd_bf16(const uint16_t* x, const float* running_mean,

@@ -10,7 +10,7 @@ import normalisation_dilated_conv1d_amd as dc
 pytestmark = pytest.mark.skipif(not __import__("os").path.exists(dc.LIB_PATH),
                                 reason="libdconv1d.so not built")
 
-EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_bf16", "prenorm_dconv1d_fwd_train",
+EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_noalloc", "prenorm_dconv1d_fwd_bf16", "prenorm_dconv1d_fwd_train",
             "prenorm_dconv1d_fwd_train_bf16", "relu_dconv1d_residual_fwd",
             "relu_dconv1d_residual_fwd_bf16", "conv1d_groupnorm_fwd",
             "dconv1d_last_error", "dconv1d_release", "dconv1d_timer_enable",
@@ -38,7 +38,8 @@ def _block(lib, x=FAKE_X, out=FAKE_OUT, N=2, C=16, L=512, d=128, eps=1e-5, b=FAK
     return getattr(lib, fn)(x, rm, FAKE_P, FAKE_P, FAKE_P, eps, W, b, out, N, C, L, d, None)
 
 
-@pytest.mark.parametrize("fn", ["prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_bf16"])
+@pytest.mark.parametrize("fn", ["prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_noalloc",
+                                "prenorm_dconv1d_fwd_bf16"])
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), dc.DCONV1D_EINVAL), (dict(out=None), dc.DCONV1D_EINVAL),
     (dict(W=None), dc.DCONV1D_EINVAL), (dict(rm=None), dc.DCONV1D_EINVAL),
