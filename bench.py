@@ -6,10 +6,14 @@ workload: the BN fold + weight repack kernel and the fused implicit-GEMM kernel,
 all inputs resident in HBM. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--workload 1|2|3|4] [--dilation D]
+                    [--no-other-workloads] [--workload 1|2|3|4] [--dilation D]
 
+The default run (workload 1) also times the other workloads after the headline one and
+adds them to the same line under "other_workloads": the dilation sweep (d = 1, 8, 512,
+2048), Conv1d+GroupNorm and the bf16-storage block, each with its step time, its
+dominant kernel's HIP-event time and that kernel's roofline fractions.
 --workload 2 (the same block at dilation D, one of 1, 8, 512, 2048), 3 (Conv1d+GroupNorm)
-and 4 (bf16 storage) time the other workloads the same way; the default, workload 1, is
+and 4 (bf16 storage) time one of them alone, as the headline; the default, workload 1, is
 the reported metric. For the block workloads,
 --bn train times the training-mode entry point (batch-statistics pass, running-stat
 update, then the same conv) and --bn external the entry point that takes an already
@@ -89,15 +93,173 @@ def cpu_baseline(w, min_seconds: float):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
+    # cores = the BLAS threads the oracle's matrix products ran on
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
                              for i in info if i.get("user_api") == "blas"})) or "unknown"
     return {"value": round(flops * reps / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"whole N=32 C=256 L=4096 d=128 workload, float64 numpy oracle, "
                       f"{reps} run(s) in {el:.1f} s",
             "cpu": cpu_model(), "blas": blas}
+
+
+def _kernel_name(workload_kind, bf16):
+    if workload_kind == "groupnorm":
+        return "conv_gn_fused_kernel<1, 4>"   # per-wave windows, 16-byte loads
+    return "conv_bf16_kernel<pair, 8 waves>" if bf16 else "conv_f32_kernel<128, BN, residual, float>"
+
+
+def setup(workload, dilation, bn, dev):
+    """Inputs resident on the device and the step of one workload: returns a dict with the
+    step function, its algorithmic flops and bytes, the config and the dtype."""
+    import torch
+
+    import normalisation_dilated_conv1d_amd as dc
+    from normalisation_dilated_conv1d_amd.inputs import (WORKLOADS, groupnorm_inputs,
+                                                          prenorm_inputs, seed_for)
+
+    wl = WORKLOADS[workload]
+    w = wl.dims
+    wname = wl.name if workload != 2 else f"{wl.name}_d{dilation}"
+    if wl.kind == "prenorm":
+        if workload == 2:
+            w = dict(w, d=dilation)
+        N, C, L, d = w["N"], w["C"], w["L"], w["d"]
+        bf16 = w["dtype"] == "bf16"
+        # the sweep's inputs are drawn per dilation, as in its parity tests
+        p = prenorm_inputs(N, C, L, seed_for(workload, d if workload == 2 else 0), bf16=bf16)
+        q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+        out = torch.empty_like(q["x"])
+        if bn == "eval":
+            fn = dc.prenorm_dconv1d_fwd_bf16 if bf16 else dc.prenorm_dconv1d_fwd
+
+            def step():
+                fn(q["x"], q["running_mean"], q["running_var"], q["gamma"], q["beta"], q["eps"],
+                   q["W"], q["b"], d, out=out)
+        elif bn == "train":
+            fn = dc.prenorm_dconv1d_fwd_train_bf16 if bf16 else dc.prenorm_dconv1d_fwd_train
+            rm, rv = q["running_mean"].clone(), q["running_var"].clone()
+            sm, si = torch.empty_like(rm), torch.empty_like(rm)
+
+            def step():
+                fn(q["x"], rm, rv, q["gamma"], q["beta"], q["eps"], 0.1, q["W"], q["b"], d,
+                   out=out, save_mean=sm, save_invstd=si)
+        else:
+            fn = dc.relu_dconv1d_residual_fwd_bf16 if bf16 else dc.relu_dconv1d_residual_fwd
+            # the caller's normalised activation, made once outside the timed region
+            xn = torch.nn.functional.batch_norm(
+                q["x"].float(), q["running_mean"], q["running_var"], q["gamma"], q["beta"],
+                training=False, eps=q["eps"]).to(q["x"].dtype).contiguous()
+
+            def step():
+                fn(xn, q["W"], q["b"], q["x"], d, out=out)
+
+        esz = 2 if bf16 else 4
+        flops = 2.0 * N * L * C * 3 * C
+        alg_bytes = esz * 2.0 * N * C * L + 4.0 * (3 * C * C + 5 * C)
+        if bn != "eval":
+            # train: the statistics pass reads x before the conv can start; external: the
+            # normalised input and the residual are separate tensors
+            alg_bytes += esz * 1.0 * N * C * L
+        config = {"workload": wname, "N": N, "C": C, "L": L, "kernel_size": 3,
+                  "dilation": d, "padding": d, "bn_mode": bn, "parallelism": "single GPU"}
+        if workload == 2:
+            # share of the counted (output step, tap) pairs whose input lies inside [0, L);
+            # the metric counts the padded ones too
+            config["valid_tap_share"] = round((L + 2 * max(L - d, 0)) / (3 * L), 4)
+    else:
+        N, C_in, C_out, T, G = w["N"], w["C_in"], w["C_out"], w["T"], w["G"]
+        p = groupnorm_inputs(N, C_in, C_out, T, seed_for(workload))
+        q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+        T_out = T + 2 * w["padding"] - 2 * w["dilation"]
+        out = torch.empty((N, C_out, T_out), device=dev)
+        bf16 = False
+
+        def step():
+            dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"],
+                                    G, w["padding"], w["dilation"], out=out)
+
+        flops = 2.0 * N * T_out * C_out * 3 * C_in
+        # one launch (every group inside one workgroup): x once, out written once, W and
+        # the affine vectors; the conv output never reaches HBM
+        alg_bytes = 4.0 * (N * C_in * T + N * C_out * T_out + 3 * C_in * C_out + 2 * C_out)
+        config = {"workload": wl.name, "N": N, "C_in": C_in, "C_out": C_out, "T": T,
+                  "num_groups": G, "kernel_size": 3, "padding": w["padding"],
+                  "dilation": w["dilation"], "parallelism": "single GPU"}
+    return {"step": step, "flops": flops, "alg_bytes": alg_bytes, "config": config,
+            "bf16": bf16, "kernel": _kernel_name(wl.kind, bf16), "out": out}
+
+
+def timed(step, steps, warmup, dev):
+    """Mean ms per step over `steps` steps after `warmup` untimed ones (HIP events on the
+    current stream), and the mean duration of the dominant kernel over another `steps`
+    steps (HIP events the library records around each launch, on its stream)."""
+    import torch
+
+    import normalisation_dilated_conv1d_amd as dc
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    with dc.KernelTimer() as kt:
+        for _ in range(steps):
+            step()
+        kern_ms, launches = kt.read()
+    return ms_per_step, kern_ms / max(launches, 1)
+
+
+def roofline(flops, alg_bytes, kern_ms, bf16, traffic):
+    """Roofline record of the dominant kernel: MFMA-bound, with the HBM side reported
+    against 8 TB/s from the algorithmic bytes and (when a current counter record exists)
+    the measured traffic."""
+    peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    k_tflops = flops / (kern_ms * 1e-3) / 1e12
+    alg_gbps = alg_bytes / (kern_ms * 1e-3) / 1e9
+    rec = {"bound": "mfma", "achieved": round(k_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+           "frac": round(k_tflops / peak, 4), "traffic": traffic,
+           "kernel_ms": round(kern_ms, 5),
+           "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes,
+           "hbm_gbps_algorithmic": round(alg_gbps, 2),
+           "hbm_frac_algorithmic": round(alg_gbps / PEAK_HBM_GBPS, 4)}
+    if traffic is not None:
+        t_gbps = traffic / (kern_ms * 1e-3) / 1e9
+        rec["hbm_gbps_traffic"] = round(t_gbps, 2)
+        rec["hbm_frac_traffic"] = round(t_gbps / PEAK_HBM_GBPS, 4)
+    return rec
+
+
+def other_workloads(dev, steps, warmup):
+    """The dilation sweep, Conv1d+GroupNorm and the bf16 block, each timed like the
+    headline workload (mean ms per step, the dominant kernel's HIP-event time and its
+    roofline fraction); parity for all of them is checked by the GPU tests."""
+    res = {}
+    for workload, dil in ((2, 1), (2, 8), (2, 512), (2, 2048), (3, None), (4, None)):
+        s = setup(workload, dil, "eval", dev)
+        ms, kms = timed(s["step"], steps, warmup, dev)
+        rec = roofline(s["flops"], s["alg_bytes"], kms, s["bf16"], measured_traffic(workload))
+        rec["kernel"] = s["kernel"]
+        res[s["config"]["workload"]] = {
+            "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
+            "value": round(s["flops"] / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "dtype": "bf16" if s["bf16"] else "f32", "config": s["config"], "roofline": rec}
+        del s
+    return res
+
+
+# The pages' own figures for this workload are back-of-envelope estimates of memory
+# traffic on a roughly 900 GB/s GPU, not measurements (pre-norm block page, design turn).
+PAGE_ESTIMATES = {"note": "page estimate, not measured",
+                  "unfused_traffic_bytes": 1.2e9, "fused_traffic_bytes": 2.7e8}
 
 
 def main():
@@ -106,6 +268,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the selected workload (the default run also times the "
+                         "dilation sweep, Conv1d+GroupNorm and the bf16 block)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
@@ -133,88 +298,16 @@ def main():
 
     import torch
 
-    import normalisation_dilated_conv1d_amd as dc
-    from normalisation_dilated_conv1d_amd.inputs import (WORKLOADS, groupnorm_inputs,
-                                                          prenorm_inputs, seed_for)
+    from normalisation_dilated_conv1d_amd.inputs import WORKLOADS
 
-    wl = WORKLOADS[args.workload]
-    w = wl.dims
-    wname = wl.name if args.workload != 2 else f"{wl.name}_d{args.dilation}"
+    if args.workload == 2 and args.dilation not in WORKLOADS[2].dims["ds"]:
+        ap.error(f"--dilation must be one of {WORKLOADS[2].dims['ds']}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if wl.kind == "prenorm":
-        if args.workload == 2:
-            if args.dilation not in w["ds"]:
-                ap.error(f"--dilation must be one of {w['ds']}")
-            w = dict(w, d=args.dilation)
-        N, C, L, d = w["N"], w["C"], w["L"], w["d"]
-        bf16 = w["dtype"] == "bf16"
-        # the sweep's inputs are drawn per dilation, as in its parity tests
-        p = prenorm_inputs(N, C, L, seed_for(args.workload, d if args.workload == 2 else 0),
-                           bf16=bf16)
-        q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
-        out = torch.empty_like(q["x"])
-        if args.bn == "eval":
-            fn = dc.prenorm_dconv1d_fwd_bf16 if bf16 else dc.prenorm_dconv1d_fwd
-
-            def step():
-                fn(q["x"], q["running_mean"], q["running_var"], q["gamma"], q["beta"], q["eps"],
-                   q["W"], q["b"], d, out=out)
-        elif args.bn == "train":
-            fn = dc.prenorm_dconv1d_fwd_train_bf16 if bf16 else dc.prenorm_dconv1d_fwd_train
-            rm, rv = q["running_mean"].clone(), q["running_var"].clone()
-            sm, si = torch.empty_like(rm), torch.empty_like(rm)
-
-            def step():
-                fn(q["x"], rm, rv, q["gamma"], q["beta"], q["eps"], 0.1, q["W"], q["b"], d,
-                   out=out, save_mean=sm, save_invstd=si)
-        else:
-            fn = dc.relu_dconv1d_residual_fwd_bf16 if bf16 else dc.relu_dconv1d_residual_fwd
-            # the caller's normalised activation, made once outside the timed region
-            xn = torch.nn.functional.batch_norm(
-                q["x"].float(), q["running_mean"], q["running_var"], q["gamma"], q["beta"],
-                training=False, eps=q["eps"]).to(q["x"].dtype).contiguous()
-
-            def step():
-                fn(xn, q["W"], q["b"], q["x"], d, out=out)
-
-        C_in = C_out = C
-        T_out = L
-        esz = 2 if bf16 else 4
-        flops = 2.0 * N * L * C * 3 * C
-        alg_bytes = esz * 2.0 * N * C * L + 4.0 * (3 * C * C + 5 * C)
-        if args.bn != "eval":
-            # train: the statistics pass reads x before the conv can start; external: the
-            # normalised input and the residual are separate tensors
-            alg_bytes += esz * 1.0 * N * C * L
-        config = {"workload": wname, "N": N, "C": C, "L": L, "kernel_size": 3,
-                  "dilation": d, "padding": d, "bn_mode": args.bn, "parallelism": "single GPU"}
-        if args.workload == 2:
-            # share of the counted (output step, tap) pairs whose input lies inside [0, L);
-            # the metric counts the padded ones too
-            config["valid_tap_share"] = round((L + 2 * max(L - d, 0)) / (3 * L), 4)
-        kernel_name = ("conv_bf16_kernel<pair>" if bf16
-                       else "conv_f32_kernel<128, BN, residual, float>")
-    else:
-        N, C_in, C_out, T, G = w["N"], w["C_in"], w["C_out"], w["T"], w["G"]
-        p = groupnorm_inputs(N, C_in, C_out, T, seed_for(args.workload))
-        q = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
-        T_out = T + 2 * w["padding"] - 2 * w["dilation"]
-        out = torch.empty((N, C_out, T_out), device=dev)
-        bf16 = False
-
-        def step():
-            dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"],
-                                    G, w["padding"], w["dilation"], out=out)
-
-        flops = 2.0 * N * T_out * C_out * 3 * C_in
-        # one launch (every group inside one workgroup): x once, out written once, W and
-        # the affine vectors; the conv output never reaches HBM
-        alg_bytes = 4.0 * (N * C_in * T + N * C_out * T_out + 3 * C_in * C_out + 2 * C_out)
-        config = {"workload": wl.name, "N": N, "C_in": C_in, "C_out": C_out, "T": T,
-                  "num_groups": G, "kernel_size": 3, "padding": w["padding"],
-                  "dilation": w["dilation"], "parallelism": "single GPU"}
-        kernel_name = "conv_gn_fused_kernel<1, 4>"   # per-wave windows, 16-byte loads
+    s = setup(args.workload, args.dilation, args.bn, dev)
+    step, flops, alg_bytes, bf16 = s["step"], s["flops"], s["alg_bytes"], s["bf16"]
+    config = s["config"]
+    wname = config["workload"]
 
     for _ in range(args.warmup):
         step()
@@ -255,6 +348,8 @@ def main():
 
     # dominant kernel alone: HIP events recorded by the library around each launch of
     # the fused conv kernel, on the stream it is launched on
+    import normalisation_dilated_conv1d_amd as dc
+
     with dc.KernelTimer() as kt:
         for _ in range(args.steps):
             step()
@@ -272,11 +367,13 @@ def main():
     peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    k_tflops = flops / (kern_ms_avg * 1e-3) / 1e12
     metric = ("fused block TFLOP/s & GB/s (N32 C256 L4096 d128) vs MI355X roofline"
               if args.workload == 1 and args.bn == "eval"
               else f"TFLOP/s & GB/s, {wname}, BN {args.bn}, vs MI355X roofline"
-              if wl.kind == "prenorm" else f"TFLOP/s & GB/s, {wname}, vs MI355X roofline")
+              if "C" in config else f"TFLOP/s & GB/s, {wname}, vs MI355X roofline")
+    rl = roofline(flops, alg_bytes, kern_ms_avg, bf16,
+                  measured_traffic(args.workload) if args.bn == "eval" else None)
+    rl["kernel"] = s["kernel"]
 
     line = {
         "metric": metric,
@@ -296,18 +393,16 @@ def main():
         "ms_per_step_median": round(warm_median, 5),
         "ms_per_step_median_cold_mall": round(cold_median, 5),
         "frac_mfma_peak": round(tflops / peak, 4),
-        "roofline": {"bound": "mfma", "achieved": round(k_tflops, 3),
-                     "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / peak, 4),
-                     "traffic": (measured_traffic(args.workload)
-                                 if args.bn == "eval" else None),
-                     "kernel": kernel_name,
-                     "kernel_ms": round(kern_ms_avg, 5),
-                     "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": alg_bytes},
+        "roofline": rl,
     }
-    if not args.no_cpu_baseline and args.workload == 1 and args.bn == "eval":
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    del s, step
+    if args.workload == 1 and args.bn == "eval":
+        line["page_traffic_estimates"] = PAGE_ESTIMATES
+        if not args.no_other_workloads:
+            line["other_workloads"] = other_workloads(dev, min(args.steps, 30),
+                                                      min(args.warmup, 20))
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(WORKLOADS[1].dims, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
