@@ -119,16 +119,22 @@ conv_f32_kernel(ConvF32Args a) {
   auto load_x = [&](int q) {
     const int c = q / 3, k = q - 3 * c;
     const int off = k * a.dil - a.pad;
+    // a row's base address is wave-uniform (scalar registers) and a lane's byte offset
+    // inside the row is one 32-bit register per column block (L_in < 2^30)
+    uint32_t boff[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       // a padded tap may read any in-range step: store_z masks it to zero
       const uint32_t ts = tap_step(t0 + l + 64 * j, off);
-      const int tsc = ts < (uint32_t)a.L_in ? (int)ts : 0;
+      boff[j] = (ts < (uint32_t)a.L_in ? ts : 0u) * (uint32_t)sizeof(XT);
+    }
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int ci = min(c * KC + RPW * w + i, a.C_in - 1);
-        xr[i * CPT + j] = to_f32(xn[ci * a.L_in + tsc]);
-      }
+    for (int i = 0; i < RPW; ++i) {
+      const int ci = min(c * KC + RPW * w + i, a.C_in - 1);
+      const char* rowp = reinterpret_cast<const char*>(xn + (size_t)ci * a.L_in);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+        xr[i * CPT + j] = to_f32(*reinterpret_cast<const XT*>(rowp + boff[j]));
     }
     if (BN) {
 #pragma unroll
@@ -144,16 +150,27 @@ conv_f32_kernel(ConvF32Args a) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int col = l + 64 * j;
-      uint32_t tkeep = tap_step(t0 + col, off) < (uint32_t)a.L_in ? 0xffffffffu : 0u;
-      asm volatile("" : "+v"(tkeep));
+      const bool in_tap = tap_step(t0 + col, off) < (uint32_t)a.L_in;
+      // With BN the staged value is med3(fma(x, scale, shift), 0, cap), cap = +inf inside
+      // the input and 0 on a padded tap: ReLU in one instruction, and an exact zero for
+      // padding. Without BN the value is x AND a mask. Both stay opaque to the optimiser.
+      uint32_t tkeep = in_tap ? 0xffffffffu : 0u;
+      float cap = in_tap ? __builtin_huge_valf() : 0.f;
+      asm volatile("" : "+v"(tkeep), "+v"(cap));
       const int pos = 64 * j + (col & 15) * 4 + ((col & 63) >> 4);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int row = RPW * w + i;
-        const uint32_t keep = (c * KC + row < a.C_in) ? tkeep : 0u;
-        float v = xr[i * CPT + j];
-        if (BN) v = fmaxf(fmaf(v, sc[i], sh[i]), 0.f);
-        dst[row * PITCH + pos] = __uint_as_float(__float_as_uint(v) & keep);
+        const float v = xr[i * CPT + j];
+        if (BN) {
+          // a padded input channel has scale = shift = 0 (every fold writes that), so its
+          // value is med3(fma(x, 0, 0), 0, cap) = 0, also for an infinite or NaN x: med3
+          // with a NaN operand returns the smallest of the other two
+          dst[row * PITCH + pos] = __builtin_amdgcn_fmed3f(fmaf(v, sc[i], sh[i]), 0.f, cap);
+        } else {
+          const uint32_t keep = (c * KC + row < a.C_in) ? tkeep : 0u;
+          dst[row * PITCH + pos] = __uint_as_float(__float_as_uint(v) & keep);
+        }
       }
     }
   };
@@ -163,7 +180,11 @@ conv_f32_kernel(ConvF32Args a) {
   auto load_w = [&](int G, f32x4 (&dst)[MB]) {
     G = min(G, n_groups - 1);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) dst[mb] = Wp4[(G * a.NCB + cb0 + mb) * 64 + l];
+    for (int mb = 0; mb < MB; ++mb) {
+      // wave-uniform base (scalar registers) plus the lane's 16-byte slot
+      const f32x4* wb = Wp4 + (size_t)(G * a.NCB + cb0 + mb) * 64;
+      dst[mb] = wb[l];
+    }
   };
   // B operands of MFMA step s (row 16*(s/4) + 4*lq + s%4).
   auto load_b = [&](const float* zb, int s, f32x4 (&dst)[NQ]) {

@@ -124,6 +124,26 @@ def test_block_padding_trap():
     assert err <= TOL_F32, err
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_block_negative_infinity_in_last_channel(bf16):
+    """x = -inf at some steps of the last input channel, C_in not a multiple of the
+    kernels' 32-channel K-chunks (the padded channels then read that row): ReLU(BN(-inf))
+    is 0 with a positive scale, so every output is finite except the residual itself."""
+    N, C, L, d = 2, 40, 300, 3
+    announce("prenorm block -inf in last channel", (N, C, L, d), "bf16", bf16)
+    p = prenorm_inputs(N, C, L, 33, bf16=bf16)
+    p["gamma"][C - 1] = p["gamma"][C - 1].abs() + 0.5
+    p["x"][:, C - 1, 10:40:3] = float("-inf")
+    got = run_block(p, d, bf16=bf16).float().cpu().numpy().astype(np.float64)
+    ref = oracle_block(p, d)
+    bad = ~np.isfinite(ref)
+    assert bad.sum() == N * len(range(10, 40, 3))
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    assert np.all(np.isfinite(got[~bad]))
+    err = maxrel(got[~bad], ref[~bad])
+    assert err <= (TOL_BF16 if bf16 else TOL_F32), err
+
+
 def test_block_zero_weights_exact():
     """W = 0: out = x + b, exactly (one float32 add)."""
     N, C, L, d = 2, 40, 300, 9
