@@ -207,47 +207,29 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     else
       return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo, 0, 0));
   };
-  // This wave's part of chunk c into registers: the whole private window, or the shared
-  // window's rows 16c + w (dst[0 .. NL)) and 16c + w + 8 (dst[NL .. 2NL)).
+  // Shared window: this wave's rows 16c + w (dst[0 .. NL)) and 16c + w + 8 (dst[NL .. 2NL))
+  // of chunk c into registers (private windows go straight into LDS: dma_x below).
   XV xa[NX], xb[NX];
   auto load_x = [&](int c, XV (&dst)[NX]) {
-    if constexpr (PRIV) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(xn + (size_t)GN_CI * c * a.T), (short)0, 4 * GN_CI * a.T,
+          const_cast<float*>(xn + (size_t)(GN_CI * c + w + 8 * h) * a.T), (short)0, 4 * a.T,
           kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) dst[i] = load_one(rs, voff[i]);
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(xn + (size_t)(GN_CI * c + w + 8 * h) * a.T), (short)0, 4 * a.T,
-            kBufferFlags);
-#pragma unroll
-        for (int i = 0; i < NL; ++i) dst[h * NL + i] = load_one(rs, voff[i]);
-      }
+      for (int i = 0; i < NL; ++i) dst[h * NL + i] = load_one(rs, voff[i]);
     }
   };
-  // shared window: columns past 64*MG (the tail of the last 16-byte load) are not stored;
-  // private: items past the 16 rows are not stored
+  // columns past 64*MG (the tail of the last 16-byte load) are not stored
   auto store_x = [&](const XV (&src)[NX], float* zb) {
-    if constexpr (PRIV) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int item = l + 64 * i;
-        if (64 * (i + 1) <= GN_CI * IPR || item < GN_CI * IPR)
-          *reinterpret_cast<XV*>(zb + wz + (item / IPR) * RS + VW * (item % IPR)) = src[i];
+        const int j = 64 * VW * i + VW * l;
+        if (64 * VW * (i + 1) <= 64 * MG || j < 64 * MG)
+          *reinterpret_cast<XV*>(zb + (w + 8 * h) * RS + j) = src[h * NL + i];
       }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          const int j = 64 * VW * i + VW * l;
-          if (64 * VW * (i + 1) <= 64 * MG || j < 64 * MG)
-            *reinterpret_cast<XV*>(zb + (w + 8 * h) * RS + j) = src[h * NL + i];
-        }
-    }
   };
   // End of a chunk: the next chunk reads what this one staged. Shared window: every wave's
   // rows, so a workgroup barrier. Private: only this wave's own area; the wave's LDS
