@@ -13,16 +13,18 @@
 // W[co][ci][k] * z[ci][t - pad + k*dil], i.e. M = C_out, N = time, K = 3*C_in.
 //
 // Work split
-//   workgroup  = one sample n, 256 output channels (co tile), TT time steps (t tile);
-//                4 waves, wave w owns output channels [64w, 64w+64) of the co tile and
-//                all TT time steps: 4 x (TT/16) MFMA 16x16 accumulator blocks.
+//   workgroup  = one sample n, 64*MB output channels (co tile: 256 or 128), TT time steps
+//                (t tile: 128 or 64); 4 waves, wave w owns output channels
+//                [16*MB*w, 16*MB*(w+1)) of the co tile and all TT time steps: MB x (TT/16)
+//                MFMA 16x16 accumulator blocks.
 //   K loop     = chunks of 32 input channels of one tap, ordered (ci-block, tap) so
 //                that the three taps of a channel block are staged back to back and hit
 //                the same L2 lines.
 //   B operand  = the activation tile z[32][TT], staged through LDS once per chunk by
 //                all 256 threads (global loads coalesced along t, BN+ReLU applied in
-//                registers, zero outside [0, L_in)), double-buffered, one barrier per
-//                chunk; the staging of chunk q+1 runs in the middle of chunk q's MFMAs.
+//                registers as one med3, zero outside [0, L_in)), double-buffered, one
+//                barrier per chunk; the staging of chunk q+1 runs in the middle of chunk
+//                q's MFMAs.
 //   A operand  = the weights, read straight from global memory into registers: the
 //                repack kernel stores them in the exact lane order of the MFMA A operand,
 //                so each lane fetches 4 consecutive K values with one 16-byte load and

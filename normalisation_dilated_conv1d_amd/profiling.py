@@ -48,11 +48,39 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments, each whitespace run collapsed to one space:
+    the code the compiler sees. String and character literals are kept as they are."""
+    out = []
+    i, n = 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(kernel: str) -> str:
+    """Digest of a kernel's sources with comments and layout ignored, so that a counter
+    record stays valid across comment-only edits and goes stale on any code change."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

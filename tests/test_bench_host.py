@@ -53,3 +53,15 @@ def test_traffic_record_lookup(workload, tmp_path, monkeypatch):
     assert bench.measured_traffic(workload) is None
     monkeypatch.setitem(bench.TRAFFIC_FILES, workload, (kernel, str(tmp_path / "missing.json")))
     assert bench.measured_traffic(workload) is None
+
+
+def test_source_digest_ignores_comments_only():
+    """Comments and layout do not change what the compiler sees; any code token does."""
+    from normalisation_dilated_conv1d_amd.profiling import strip_comments
+    base = 'int f(int a) {\n  // twice\n  return 2 * a; /* a */\n}\nconst char* s = "x // y";\n'
+    reworded = 'int f(int a) {   // doubles a\n  return 2 * a;\n}\n/* the literal */\nconst char* s = "x // y";'
+    assert strip_comments(base) == strip_comments(reworded)
+    assert strip_comments(base) != strip_comments(base.replace("2 * a", "3 * a"))
+    # comment markers inside string literals are code
+    assert strip_comments(base) != strip_comments(base.replace('"x // y"', '"x "'))
+    assert strip_comments("a/**/b") == "a b"
