@@ -230,7 +230,8 @@ conv_bf16_kernel(ConvF32Args a) {
   // nearest even), exactly 0 in the time padding; 8 consecutive rows of one column go to
   // LDS with one 16-byte write. `get(i)` returns row i of the column as float, converted
   // straight from the loaded bits. Channels past C_in need no mask: their folded scale
-  // and shift are 0, so z = max(0*x + 0, 0) = 0 for the (finite) clamped load.
+  // and shift are 0, so z = max(0*x + 0, 0) = 0 for the clamped load, also when it is
+  // infinite or NaN (max drops a NaN operand).
   auto stage_column = [&](auto&& get, int col, uint32_t tkeep, uint16_t* dst) {
 #pragma unroll
     for (int half = 0; half < RPW / 8; ++half) {
