@@ -59,9 +59,11 @@ extern "C" {
 #endif
 
 #define DCONV1D_OK 0
-/* A required pointer is NULL, a size is out of range (N < 0, C < 1, L < 1, d < 1,
- * C_out % num_groups != 0, T_out < 1, eps < 0 or NaN), or an index would not fit the
- * library's 32-bit per-sample indexing (C*L >= 2^31). */
+/* A required pointer is NULL, a size is out of range (N < 0; a channel count below 1 or
+ * above 16384; L outside [1, 2^30) for the block, T or padding outside [1, 2^29) /
+ * [0, 2^29) for Conv1d + GroupNorm; d < 1; C_out % num_groups != 0; T_out < 1; eps < 0,
+ * infinite or NaN), or an index would not fit the library's 32-bit per-sample indexing
+ * (C*L >= 2^31). */
 #define DCONV1D_EINVAL -1
 /* `out` overlaps `x`. The kernels read x taps belonging to neighbouring output tiles
  * while other tiles are already writing out, so in-place operation is not supported. */
