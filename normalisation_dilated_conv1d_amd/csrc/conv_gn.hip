@@ -288,9 +288,6 @@ conv_gn_fused_kernel(GnFusedArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // one chunk: the weights of chunk c + 1 and the x of chunk c + 2 go out, chunk c
-  // computes from buffer zc, then chunk c + 1's x (loaded a chunk ago) goes to buffer zn
-  // (last read by chunk c - 1, finished before the previous chunk_sync)
   // private windows: chunk c's window straight into this wave's area of buffer zb by
   // buffer->LDS loads; load i covers items 64i .. 64i + 63, i.e. floats VW*64*i on
   auto dma_x = [&](int c, float* zb) {
@@ -300,6 +297,8 @@ conv_gn_fused_kernel(GnFusedArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) buffer_to_lds<VW>(rs, zb + wz + 64 * VW * i, voff[i]);
   };
+  // private windows, one chunk: the weights of chunk c + 1 and, into buffer zn (last read
+  // by chunk c - 1), the window of chunk c + 1 go out; chunk c computes from buffer zc
   auto chunk_dma = [&](int c, const float* zc, float* zn, const float (&wc)[12],
                        float (&w1)[12]) {
     load_w(c + 1, w1);
@@ -308,6 +307,9 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     compute(zc, wc);
     chunk_sync();
   };
+  // shared window, one chunk: the weights of chunk c + 1 and the x of chunk c + 2 go out,
+  // chunk c computes from buffer zc, then chunk c + 1's x (loaded a chunk ago) goes to
+  // buffer zn (last read by chunk c - 1, finished before the previous chunk_sync)
   auto chunk = [&](int c, const float* zc, float* zn, const float (&wc)[12], float (&w1)[12],
                    XV (&x2)[NX], const XV (&x1)[NX]) {
     load_w(c + 1, w1);
