@@ -75,12 +75,17 @@ def strip_comments(src: str) -> str:
 
 
 def source_digest(kernel: str) -> str:
-    """Digest of a kernel's sources with comments and layout ignored, so that a counter
-    record stays valid across comment-only edits and goes stale on any code change."""
+    """Digest of a kernel's sources with comments and layout ignored, plus any compile flags
+    given to those files alone, so that a counter record stays valid across comment-only
+    edits and goes stale on any change to the code or to how it is compiled."""
+    from normalisation_dilated_conv1d_amd.build import FILE_FLAGS
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(strip_comments(f.read()).encode())
+        extra = FILE_FLAGS.get(os.path.basename(rel))
+        if extra:
+            h.update(("\0flags:" + " ".join(extra)).encode())
     return h.hexdigest()
 
 

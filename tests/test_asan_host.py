@@ -22,7 +22,7 @@ def test_abi_validation_under_asan(tmp_path):
     csrc = os.path.join(ROOT, "normalisation_dilated_conv1d_amd", "csrc")
     lib = tmp_path / "libdconv1d.so"
     asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
-    build = [HIPCC, *HIP_FLAGS, *asan, "-g", f"-I{ROOT}/include", f"-I{csrc}",
+    build = [HIPCC, *HIP_FLAGS, "-shared", *asan, "-g", f"-I{ROOT}/include", f"-I{csrc}",
              *sorted(glob.glob(os.path.join(csrc, "*.hip"))), "-o", str(lib)]
     r = subprocess.run(build, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-3000:]

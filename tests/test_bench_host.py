@@ -65,3 +65,15 @@ def test_source_digest_ignores_comments_only():
     # comment markers inside string literals are code
     assert strip_comments(base) != strip_comments(base.replace('"x // y"', '"x "'))
     assert strip_comments("a/**/b") == "a b"
+
+
+def test_source_digest_covers_per_file_flags(monkeypatch):
+    """A compile flag given to one kernel's source changes that kernel's machine code, so it
+    makes that kernel's counter records stale and leaves the others valid."""
+    from normalisation_dilated_conv1d_amd import build
+    before = {k: source_digest(k) for k in ("conv_f32_kernel", "conv_gn_fused_kernel")}
+    flags = dict(build.FILE_FLAGS)
+    flags["conv_f32.hip"] = flags.get("conv_f32.hip", []) + ["-mllvm", "-some-other-choice"]
+    monkeypatch.setattr(build, "FILE_FLAGS", flags)
+    assert source_digest("conv_f32_kernel") != before["conv_f32_kernel"]
+    assert source_digest("conv_gn_fused_kernel") == before["conv_gn_fused_kernel"]
