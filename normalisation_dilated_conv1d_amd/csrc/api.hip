@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -147,12 +148,13 @@ class WorkspaceUse {
 // prenorm_dconv1d_fwd_noalloc keeps its folded BN vectors and repacked weights in this
 // fixed device array instead of the workspace, so that it never allocates. It is sized
 // for the float32 layout prenorm_common uses (scale, shift, repacked W, each 256-byte
-// aligned) at C = kNoallocMaxC: 2 KiB + 2 KiB + 3 MiB. Every device the library runs on
+// aligned) at C = kNoallocMaxC: 2 KiB + 2 KiB + 4 MiB (the four Winograd transforms;
+// the direct kernel's three taps take 3 MiB). Every device the library runs on
 // holds its own copy until the process ends. In host code `scratch` names a host-side
 // stand-in, not device memory: the device address comes from hipGetSymbolAddress, looked
 // up once per device (with that device current) and kept in g_scratch_ptr.
 constexpr int64_t kNoallocMaxC = 512;
-constexpr size_t kScratchBytes = 2 * (4 * kNoallocMaxC) + 3 * 4 * size_t(kNoallocMaxC) * kNoallocMaxC;
+constexpr size_t kScratchBytes = 2 * (4 * kNoallocMaxC) + 4 * 4 * size_t(kNoallocMaxC) * kNoallocMaxC;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];
@@ -199,6 +201,14 @@ void timer_end(int slot, hipStream_t s) {
   if (slot < 0) return;
   std::lock_guard<std::mutex> lock(g_timer_mu);
   (void)hipEventRecord(g_timer.ev[2 * slot + 1], s);
+}
+
+// ---------------------------------------------------------------- algorithm choice
+// DCONV1D_NO_WINOGRAD=1 in the environment (read at every call) makes the float32 block
+// use the direct three-tap kernel for every dilation, e.g. to compare the two.
+bool winograd_disabled() {
+  const char* v = std::getenv("DCONV1D_NO_WINOGRAD");
+  return v != nullptr && v[0] != '\0' && v[0] != '0';
 }
 
 // ---------------------------------------------------------------- shared checks
@@ -296,16 +306,23 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   }
 
   const int Ci = (int)C, Li = (int)L;
-  // bf16 storage runs the bf16-MFMA kernel: 64-channel K-chunks, 128-step time tiles
-  // (a 256- or 512-channel tile), float32 the tile conv_f32_tile picks; the repacked
-  // weights are padded to whole channel tiles
+  // d >= L: both outer taps are always in the padding; d = L gives the same result and
+  // keeps every tap offset inside int range.
+  const int d_eff = (int)std::min<int64_t>(d, L);
+  // float32 storage takes the Winograd kernel when the dilation divides 32 or is a
+  // multiple of it (32 output pairs and 256 channels per tile), else the direct kernel
+  // with the tile conv_f32_tile picks; bf16 storage runs the bf16-MFMA kernel: 64-channel
+  // K-chunks, 128-step time tiles (a 256- or 512-channel tile). The repacked weights are
+  // padded to whole channel tiles.
+  const bool wino = !bf16 && wino_fits(Li, d_eff) && !winograd_disabled();
   const int Cin_pad = round_up(Ci, bf16 ? CIN_PAD_BF16 : KC);
   const int co_tile_bf16 = bf16 ? conv_bf16_co_tile(N, Li, Ci) : 0;
   const int Cout_pad = round_up(Ci, bf16 ? co_tile_bf16 : CO_TILE_F32);
   const ConvTile tile = bf16 ? ConvTile{TILE_T_BF16, co_tile_bf16 / 64}
-                             : conv_f32_tile(Li, (int)std::min<int64_t>(N, kMaxIndex), Ci);
+                        : wino ? ConvTile{0, CO_TILE_F32 / 64}
+                               : conv_f32_tile(Li, (int)std::min<int64_t>(N, kMaxIndex), Ci);
   const int n_ct = (Ci + tile.co_tile() - 1) / tile.co_tile();
-  const int n_tt = (Li + tile.tt - 1) / tile.tt;
+  const int n_tt = wino ? wino_pair_tiles(Li, d_eff) : (Li + tile.tt - 1) / tile.tt;
   if (N * n_tt * n_ct > kMaxIndex)
     return fail(DCONV1D_EINVAL, "grid of %lld workgroups is too large",
                 (long long)(N * n_tt * n_ct));
@@ -313,11 +330,8 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
     return fail(DCONV1D_EINVAL, "statistics grid is too large");
   if (N == 0) return DCONV1D_OK;
 
-  // d >= L: both outer taps are always in the padding; d = L gives the same result and
-  // keeps every tap offset inside int range.
-  const int d_eff = (int)std::min<int64_t>(d, L);
-
-  const size_t wp_bytes = (bf16 ? 2 : 4) * 3 * (size_t)Cin_pad * Cout_pad;
+  // repacked weights: three taps, or the four Winograd transforms
+  const size_t wp_bytes = (bf16 ? 2 : 4) * (wino ? 4 : 3) * (size_t)Cin_pad * Cout_pad;
   const size_t off_scale = 0;
   const size_t off_shift = align256(off_scale + sizeof(float) * Cin_pad);
   const size_t off_wp = align256(off_shift + sizeof(float) * Cin_pad);
@@ -353,8 +367,11 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   const float* fold_gamma = norm == Norm::External ? nullptr : gamma;
   e = bf16 ? launch_prep_bf16(W, Ci, Ci, Cout_pad, Cin_pad, Wp, running_mean, running_var,
                               fold_gamma, beta, eps, fold_scale, fold_shift, stream)
-           : launch_prep_f32(W, Ci, Ci, Cout_pad, Cin_pad, static_cast<float*>(Wp), running_mean,
-                             running_var, fold_gamma, beta, eps, fold_scale, fold_shift, stream);
+      : wino ? launch_prep_wino(W, Ci, Ci, Cout_pad, Cin_pad, static_cast<float*>(Wp),
+                                running_mean, running_var, fold_gamma, beta, eps, fold_scale,
+                                fold_shift, stream)
+             : launch_prep_f32(W, Ci, Ci, Cout_pad, Cin_pad, static_cast<float*>(Wp), running_mean,
+                               running_var, fold_gamma, beta, eps, fold_scale, fold_shift, stream);
   if (e != hipSuccess) return hip_fail(e, "prep kernel launch");
 
   ConvF32Args a{};
@@ -374,12 +391,13 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   a.pad = d_eff;
   a.dil = d_eff;
   a.NCB = Cout_pad / 16;
-  a.Q = 3 * Cin_pad / (bf16 ? KC_BF16 : KC);
+  a.Q = wino ? Cin_pad / KC : 3 * Cin_pad / (bf16 ? KC_BF16 : KC);
   a.n_tt = n_tt;
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
   e = bf16 ? launch_conv_bf16(a, tile.co_tile(), stream)
-           : launch_conv_f32(a, tile, EPI_RESIDUAL, stream);
+      : wino ? launch_conv_wino(a, stream)
+             : launch_conv_f32(a, tile, EPI_RESIDUAL, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
   return DCONV1D_OK;

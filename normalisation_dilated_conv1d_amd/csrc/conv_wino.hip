@@ -1,0 +1,338 @@
+// Float32 kernel for the pre-norm residual block (POPCORNBENCH "Kimi-K2.6__l2_p12", first
+// turn: out = x + b + Conv1d_{k=3, dilation d, padding d}(ReLU(BN(x)))) by Winograd
+// F(2,3) along the dilation lattice.
+//
+// Two outputs d apart share three of their four inputs. With z = ReLU(BN(x)) (zero
+// outside [0, L)), taps g0, g1, g2 and the inputs v0..v3 = z(t - d), z(t), z(t + d),
+// z(t + 2d) of the output pair (t, t + d):
+//   V0 = v0 - v2,  V1 = v1 + v2,  V2 = v2 - v1,  V3 = v1 - v3
+//   U0 = g0,  U1 = (g0 + g1 + g2) / 2,  U2 = (g0 - g1 + g2) / 2,  U3 = g2
+//   M_j = sum over input channels of U_j * V_j
+//   y(t) = M0 + M1 + M2,  y(t + d) = M1 - M2 - M3,
+// which is the direct three-tap sum exactly (up to rounding), with four products per pair
+// and input channel instead of six: the four M_j are four GEMMs of K = C_in, so the
+// kernel runs 2/3 of the direct conv's MFMA work.
+//
+// Pairs. Output step t = 2d*b + r (r < d) pairs with t + d. A tile of 32 pairs is either
+// 32 consecutive r of one super-block b (d a multiple of 32: outputs [T0, T0 + 32) and
+// [T0 + d, T0 + d + 32)) or 32/d whole super-blocks (d dividing 32: outputs
+// [T0, T0 + 64)). With D = min(d, 32), pair c of the tile (0..31) has first step
+//   t0(c) = T0 + 2D*(c / D) + c % D.
+//
+// Work split
+//   workgroup  = one sample n, 256 output channels, 32 pairs (64 output steps); 4 waves,
+//                wave w owns output channels [64w, 64w + 64): for each of the four
+//                transforms j, 4 x 2 MFMA 16x16 accumulator blocks (128 registers).
+//   K loop     = chunks of 32 input channels (no taps: they are inside the transform),
+//                8 MFMA steps of K = 4 each, 32 MFMAs per step.
+//   B operand  = V_j[32 rows][32 pairs] staged through LDS per chunk by all 256 threads:
+//                each thread loads 4 (row, pair) items' four lattice inputs, applies
+//                BN+ReLU (med3(fma(x, scale, shift), 0, cap), cap = 0 outside the input),
+//                forms V0..V3 and writes them with one 16-byte store; double-buffered, one
+//                barrier per chunk, the next chunk staged in the middle of the current
+//                one's MFMAs. A row holds, for pair c, the four V_j at
+//                64*(c/16) + 4*(c%16) + j, so a lane's B values of one MFMA step (pairs
+//                l%16 and 16 + l%16, all four j) are two 16-byte LDS reads.
+//   A operand  = U_j from the repack of prep_wino_kernel, one 16-byte load per (step,
+//                16-channel block) holding the four j, one step ahead.
+//   Epilogue   = y(t0), y(t0 + d) from the four accumulator sets in registers, then as in
+//                the direct kernel: through LDS so that a lane owns 4 consecutive steps,
+//                + bias + residual (16-byte loads), non-temporal 16-byte stores.
+//   MFMA       = v_mfma_f32_16x16x4_f32 (float32 products and accumulation).
+//
+// The K-row permutation inside a chunk (r = 16g + 4q + u) and the XCD-aware workgroup order
+// are those of the direct kernel (conv_f32.hip).
+
+#include "internal.h"
+
+namespace dconv1d {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WPAIRS = 32;                // output pairs per workgroup
+constexpr int WPITCH = 4 * WPAIRS + 4;    // floats per staged row (four V_j per pair)
+constexpr int WEP = 2 * WPAIRS + 4;       // floats per epilogue row (64 output steps)
+constexpr int WMB = 4;                    // 16-channel blocks per wave
+constexpr int WNB = WPAIRS / 16;          // 16-pair blocks per wave
+constexpr int WRPL = KC * WPAIRS / NTHREADS;   // staged (row, pair) items per thread (4)
+
+// first output step of pair tile pt
+__device__ __forceinline__ int wino_tile_start(int pt, int d) {
+  if (d >= 32) {
+    const int per = d >> 5;
+    return 2 * d * (pt / per) + 32 * (pt % per);
+  }
+  return 64 * pt;
+}
+
+}  // namespace
+
+bool wino_fits(int L, int dil) {
+  return L >= 1 && L < (1 << 28) && dil >= 1 && ((dil % 32) == 0 || (32 % dil) == 0);
+}
+
+int wino_pair_tiles(int L, int dil) {
+  const long long blocks = ((long long)L + 2LL * dil - 1) / (2LL * dil);   // super-blocks
+  const long long pairs = blocks * dil;
+  return (int)((pairs + WPAIRS - 1) / WPAIRS);
+}
+
+__global__ void __launch_bounds__(NTHREADS, 2)
+conv_wino_kernel(ConvF32Args a) {
+  constexpr int CO_TILE = 64 * WMB;
+  // two named staging buffers (see conv_f32.hip); the epilogue reuses them
+  __shared__ __attribute__((aligned(16))) float zs0[KC * WPITCH];
+  __shared__ __attribute__((aligned(16))) float zs1[KC * WPITCH];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int lq = l >> 4;
+  const int l16 = l & 15;
+
+  const int nwg = gridDim.x;
+  const int b = blockIdx.x;
+  const int per = nwg >> 3, rem = nwg & 7, xcd = b & 7;
+  const int logical = xcd * per + min(xcd, rem) + (b >> 3);
+  const int ct = __builtin_amdgcn_readfirstlane(logical % a.n_ct);
+  const int rest = logical / a.n_ct;
+  const int pt = __builtin_amdgcn_readfirstlane(rest % a.n_tt);
+  const int n = __builtin_amdgcn_readfirstlane(rest / a.n_tt);
+
+  const int d = a.dil;
+  const int L = a.L_in;
+  const int T0 = __builtin_amdgcn_readfirstlane(wino_tile_start(pt, d));
+  const int D = min(d, 32);                 // a power of two
+  const int lgD = __builtin_ctz(D);
+
+  const float* __restrict__ xn = reinterpret_cast<const float*>(a.x) + (size_t)n * a.C_in * L;
+  const f32x4* __restrict__ Up4 = reinterpret_cast<const f32x4*>(a.Wp);
+  const int cb0 = (ct * CO_TILE) / 16 + WMB * w;
+
+  f32x4 acc[4][WMB][WNB];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][mb][nb][r] = 0.f;
+
+  // Staging geometry of this lane: pair c = l % 32 of the tile, rows 8w + 2i + l/32
+  // (i = 0..3) of each chunk. The four lattice steps of the pair and their caps are the
+  // same for every chunk.
+  const int c = l & 31;
+  const int hrow = l >> 5;
+  const int t0c = T0 + ((c >> lgD) << (lgD + 1)) + (c & (D - 1));
+  uint32_t toff[4];                         // byte offsets inside a row
+  float cap[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = t0c + (m - 1) * d;      // |t| < 2^30: L, d < 2^28
+    const bool in = t >= 0 && t < L;
+    // an outside step loads any in-range step: its cap makes it zero
+    toff[m] = 4u * (uint32_t)(in ? t : 0);
+    cap[m] = in ? __builtin_huge_valf() : 0.f;
+    asm volatile("" : "+v"(cap[m]));
+  }
+  const int zpos = 64 * (c >> 4) + 4 * (c & 15);   // LDS position of the pair in a row
+
+  float xr[WRPL][4];
+  float sc[WRPL], sh[WRPL];
+  auto load_x = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < WRPL; ++i) {
+      // a padded input channel loads the last real row: its scale and shift are 0
+      const int rb = min(KC * q + 8 * w + 2 * i, a.C_in - 1);            // wave-uniform
+      const int rl = min(KC * q + 8 * w + 2 * i + hrow, a.C_in - 1);     // this lane's
+      // the row's base address is wave-uniform (scalar registers); the lane adds one row
+      // (or none) and its step, in bytes: below 2^31 as L < 2^28
+      const char* rowp = reinterpret_cast<const char*>(xn + (size_t)rb * L);
+      const uint32_t ro = (uint32_t)(rl - rb) * 4u * (uint32_t)L;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        xr[i][m] = *reinterpret_cast<const float*>(rowp + (ro + toff[m]));
+      sc[i] = a.scale[KC * q + 8 * w + 2 * i + hrow];
+      sh[i] = a.shift[KC * q + 8 * w + 2 * i + hrow];
+    }
+  };
+  auto store_z = [&](float* dst) {
+#pragma unroll
+    for (int i = 0; i < WRPL; ++i) {
+      float z[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        z[m] = __builtin_amdgcn_fmed3f(fmaf(xr[i][m], sc[i], sh[i]), 0.f, cap[m]);
+      f32x4 v;
+      v[0] = z[0] - z[2];
+      v[1] = z[1] + z[2];
+      v[2] = z[2] - z[1];
+      v[3] = z[1] - z[3];
+      *reinterpret_cast<f32x4*>(dst + (8 * w + 2 * i + hrow) * WPITCH + zpos) = v;
+    }
+  };
+  // A operands of MFMA step s of chunk q: one float4 (U0..U3) per 16-channel block
+  const int Q = a.Q;
+  auto load_a = [&](int q, int s, f32x4 (&dst)[WMB]) {
+    q = min(q, Q - 1);
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      const f32x4* ub = Up4 + (size_t)((8 * q + s) * a.NCB + cb0 + mb) * 64;
+      dst[mb] = ub[l];
+    }
+  };
+  // B operands of MFMA step s (row 16*(s/4) + 4*lq + s%4): pairs l16 and 16 + l16
+  auto load_b = [&](const float* zb, int s, f32x4 (&dst)[WNB]) {
+    const float* p = zb + (16 * (s >> 2) + 4 * lq + (s & 3)) * WPITCH + 4 * l16;
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) dst[nb] = *reinterpret_cast<const f32x4*>(p + 64 * nb);
+  };
+
+  f32x4 au[2][WMB];
+  f32x4 bv[2][WNB];
+
+  auto compute = [&](const float* zb, int q, auto&& mid) {
+    load_b(zb, 0, bv[0]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      // the next step's operands (the next chunk's first A at the last step) go out first
+      load_a(s + 1 < 8 ? q : q + 1, (s + 1) & 7, au[(s + 1) & 1]);
+      if (s + 1 < 8) load_b(zb, s + 1, bv[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < WNB; ++nb)
+            acc[j][mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                au[s & 1][mb][j], bv[s & 1][nb][j], acc[j][mb][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 3) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  load_a(0, 0, au[0]);
+  load_x(0);
+  store_z(zs0);
+  __syncthreads();
+  int q = 0;
+  for (; q + 1 < Q; q += 2) {
+    load_x(q + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(zs0, q, [&] { store_z(zs1); });
+    __syncthreads();
+    const int qn = min(q + 2, Q - 1);
+    load_x(qn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(zs1, q + 1, [&] { store_z(zs0); });
+    __syncthreads();
+  }
+  if (q < Q) compute(zs0, q, [] {});
+
+  // Epilogue. Register r of block (j, mb, nb) holds M_j of output channel 16mb + 4lq + r
+  // (within the wave's 64) and pair 16nb + l16; y(t0) = (M0 + M1) + M2 and
+  // y(t0 + d) = (M1 - M2) - M3. Output column o of the tile (0..63, increasing step) of
+  // pair c: o0 = 2D*(c / D) + c % D and o0 + D; its step is T0 + o, or T0 + d + (o - 32)
+  // for o >= 32 when d > 32.
+  float* outn = reinterpret_cast<float*>(a.out) + (size_t)n * a.C_out * L;
+  const float* resn = reinterpret_cast<const float*>(a.residual) + (size_t)n * a.C_out * L;
+  const int co_w = ct * CO_TILE + 16 * WMB * w;
+  const int skip = d > 32 ? d - 32 : 0;
+  const bool vec_epi = ((L & 3) == 0) &&
+                       (((reinterpret_cast<uintptr_t>(a.out) |
+                          reinterpret_cast<uintptr_t>(a.residual)) & 15) == 0);
+  if (vec_epi) {
+    // every wave has finished reading its last B operands; each wave then uses its own
+    // 16 x WEP tile, and its LDS accesses complete in order
+    __syncthreads();
+    float* ep = (w < 2 ? zs0 : zs1) + (w & 1) * (16 * WEP);
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int cc = 16 * nb + l16;
+        const int o0 = ((cc >> lgD) << (lgD + 1)) + (cc & (D - 1));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float m0 = acc[0][mb][nb][r], m1 = acc[1][mb][nb][r];
+          const float m2 = acc[2][mb][nb][r], m3 = acc[3][mb][nb][r];
+          ep[(4 * lq + r) * WEP + o0] = (m0 + m1) + m2;
+          ep[(4 * lq + r) * WEP + o0 + D] = (m1 - m2) - m3;
+        }
+      }
+      // 16 rows x 16 four-step chunks, 4 per lane; residual and bias loads (clamped
+      // in-bounds; L is a multiple of 4, so a clamped chunk start is too) before any use
+      f32x4 rv[4];
+      float bia[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int item = l + 64 * i;
+        const int row = item >> 4, o = 4 * (item & 15);
+        const int t = T0 + o + (o >= 32 ? skip : 0);
+        const int coc = min(co_w + 16 * mb + row, a.C_out - 1);
+        const int tcl = min(t, L - 4);
+        rv[i] = *reinterpret_cast<const f32x4*>(resn + (size_t)coc * L + tcl);
+        bia[i] = a.bias ? a.bias[coc] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int item = l + 64 * i;
+        const int row = item >> 4, o = 4 * (item & 15);
+        const int t = T0 + o + (o >= 32 ? skip : 0);
+        const int co = co_w + 16 * mb + row;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ep + row * WEP + o);
+        f32x4 res;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = v[e] + bia[i] + rv[i][e];
+        // t and L are multiples of 4: the 4 steps are all in range or all out
+        if (co < a.C_out && t < L)
+          __builtin_nontemporal_store(res, reinterpret_cast<f32x4*>(outn + (size_t)co * L + t));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int co = co_w + 16 * mb + 4 * lq + r;
+        const int coc = min(co, a.C_out - 1);
+        const float bco = a.bias ? a.bias[coc] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) {
+          const int cc = 16 * nb + l16;
+          const int ta = T0 + ((cc >> lgD) << (lgD + 1)) + (cc & (D - 1));
+          const int tb = ta + d;
+          const float m0 = acc[0][mb][nb][r], m1 = acc[1][mb][nb][r];
+          const float m2 = acc[2][mb][nb][r], m3 = acc[3][mb][nb][r];
+          const float ra = resn[(size_t)coc * L + min(ta, L - 1)];
+          const float rb = resn[(size_t)coc * L + min(tb, L - 1)];
+          if (co < a.C_out && ta < L)
+            __builtin_nontemporal_store(((m0 + m1) + m2) + bco + ra, &outn[(size_t)co * L + ta]);
+          if (co < a.C_out && tb < L)
+            __builtin_nontemporal_store(((m1 - m2) - m3) + bco + rb, &outn[(size_t)co * L + tb]);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_conv_wino(const ConvF32Args& a, hipStream_t stream) {
+  const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.scale == nullptr || a.C_in != a.C_out || a.L_in != a.L_out || a.pad != a.dil ||
+      !wino_fits(a.L_in, a.dil) || a.n_tt != wino_pair_tiles(a.L_in, a.dil) ||
+      a.NCB * 16 < a.n_ct * 64 * WMB || a.Q * KC < a.C_in)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(conv_wino_kernel, dim3((unsigned)nwg), dim3(NTHREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dconv1d

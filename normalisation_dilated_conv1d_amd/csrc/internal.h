@@ -62,6 +62,18 @@ struct ConvTile {
 ConvTile conv_f32_tile(int L_out, int N, int C_out);
 hipError_t launch_conv_f32(const ConvF32Args& a, ConvTile tile, int epilogue, hipStream_t stream);
 
+// prep.hip: BN fold + the Winograd weight transform, [Cin_pad/4 steps][Cout_pad/16][64] x 4
+hipError_t launch_prep_wino(const float* W, int C_out, int C_in, int Cout_pad, int Cin_pad,
+                            float* Up, const float* running_mean, const float* running_var,
+                            const float* gamma, const float* beta, float eps, float* scale,
+                            float* shift, hipStream_t stream);
+// conv_wino.hip: the float32 block by Winograd F(2,3) along the dilation lattice, for a
+// dilation that divides 32 or is a multiple of it (and L_in < 2^28); 32 output pairs per
+// workgroup, a.n_tt = wino_pair_tiles(L, d), a.Q = Cin_pad / KC
+bool wino_fits(int L, int dil);
+int wino_pair_tiles(int L, int dil);
+hipError_t launch_conv_wino(const ConvF32Args& a, hipStream_t stream);
+
 // conv_bf16.hip: 64-channel K-chunks, input channels padded to a multiple of 128 (an
 // even chunk count), 128 time steps per tile
 constexpr int KC_BF16 = 64;
