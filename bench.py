@@ -36,8 +36,8 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 # committed PMC traffic records of the dominant kernel, per workload (eval-mode BN for the
 # block workloads)
 TRAFFIC_FILES = {
-    1: ("conv_f32_kernel", os.path.join(ROOT, "profiles",
-                                        "traffic_conv_f32_prenorm_N32_C256_L4096_d128.json")),
+    1: ("conv_wino_kernel", os.path.join(ROOT, "profiles",
+                                         "traffic_conv_wino_prenorm_N32_C256_L4096_d128.json")),
     4: ("conv_bf16_kernel", os.path.join(ROOT, "profiles",
                                          "traffic_conv_bf16_prenorm_N16_C512_L16384_d128.json")),
     3: ("conv_gn_fused_kernel",
@@ -105,10 +105,22 @@ def cpu_baseline(w, min_seconds: float):
             "cpu": cpu_model(), "blas": blas}
 
 
-def _kernel_name(workload_kind, bf16):
+def _kernel_name(workload_kind, bf16, winograd=False):
     if workload_kind == "groupnorm":
         return "conv_gn_fused_kernel<1, 4>"   # per-wave windows, 16-byte loads
-    return "conv_bf16_kernel<pair, 8 waves>" if bf16 else "conv_f32_kernel<128, BN, residual, float>"
+    if bf16:
+        return "conv_bf16_kernel<pair, 8 waves>"
+    return "conv_wino_kernel (Winograd F(2,3))" if winograd else "conv_f32_kernel<128, BN, residual, float>"
+
+
+def winograd_mfma_flops(N, C, L, d):
+    """Multiply-add work the Winograd kernel runs on the matrix cores for a float32 block:
+    four GEMMs over (output channels padded to 256) x (input channels padded to 32) x
+    (output pairs, in tiles of 32), two flops per multiply-add."""
+    d = min(d, L)
+    pairs = -(-L // (2 * d)) * d
+    pairs_run = -(-pairs // 32) * 32
+    return 8.0 * N * (-(-C // 256) * 256) * (-(-C // 32) * 32) * pairs_run
 
 
 def setup(workload, dilation, bn, dev):
@@ -158,13 +170,16 @@ def setup(workload, dilation, bn, dev):
 
         esz = 2 if bf16 else 4
         flops = 2.0 * N * L * C * 3 * C
+        winograd = (not bf16) and dc.dconv1d_block_method(L, d) == dc.DCONV1D_METHOD_WINOGRAD
+        mfma_flops = winograd_mfma_flops(N, C, L, d) if winograd else flops
         alg_bytes = esz * 2.0 * N * C * L + 4.0 * (3 * C * C + 5 * C)
         if bn != "eval":
             # train: the statistics pass reads x before the conv can start; external: the
             # normalised input and the residual are separate tensors
             alg_bytes += esz * 1.0 * N * C * L
         config = {"workload": wname, "N": N, "C": C, "L": L, "kernel_size": 3,
-                  "dilation": d, "padding": d, "bn_mode": bn, "parallelism": "single GPU"}
+                  "dilation": d, "padding": d, "bn_mode": bn, "parallelism": "single GPU",
+                  "conv_method": "winograd_f2_3" if winograd else "direct_3tap"}
         if workload == 2:
             # share of the counted (output step, tap) pairs whose input lies inside [0, L);
             # the metric counts the padded ones too
@@ -182,14 +197,16 @@ def setup(workload, dilation, bn, dev):
                                     G, w["padding"], w["dilation"], out=out)
 
         flops = 2.0 * N * T_out * C_out * 3 * C_in
+        winograd, mfma_flops = False, flops
         # one launch (every group inside one workgroup): x once, out written once, W and
         # the affine vectors; the conv output never reaches HBM
         alg_bytes = 4.0 * (N * C_in * T + N * C_out * T_out + 3 * C_in * C_out + 2 * C_out)
         config = {"workload": wl.name, "N": N, "C_in": C_in, "C_out": C_out, "T": T,
                   "num_groups": G, "kernel_size": 3, "padding": w["padding"],
                   "dilation": w["dilation"], "parallelism": "single GPU"}
-    return {"step": step, "flops": flops, "alg_bytes": alg_bytes, "config": config,
-            "bf16": bf16, "kernel": _kernel_name(wl.kind, bf16), "out": out}
+    return {"step": step, "flops": flops, "mfma_flops": mfma_flops, "alg_bytes": alg_bytes,
+            "config": config, "bf16": bf16, "kernel": _kernel_name(wl.kind, bf16, winograd),
+            "out": out}
 
 
 def timed(step, steps, warmup, dev):
@@ -218,16 +235,23 @@ def timed(step, steps, warmup, dev):
     return ms_per_step, kern_ms / max(launches, 1)
 
 
-def roofline(flops, alg_bytes, kern_ms, bf16, traffic):
+def roofline(flops, alg_bytes, kern_ms, bf16, traffic, mfma_flops=None):
     """Roofline record of the dominant kernel: MFMA-bound, with the HBM side reported
     against 8 TB/s from the algorithmic bytes and (when a current counter record exists)
-    the measured traffic."""
+    the measured traffic. `achieved` and `frac` count the direct conv's nominal flops
+    (2*N*L*C_out*3*C_in); the Winograd kernel runs 2/3 of them on the matrix cores, so
+    `mfma_executed_frac` is its use of the matrix cores and `frac` may exceed it."""
     peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    mfma_flops = flops if mfma_flops is None else mfma_flops
     k_tflops = flops / (kern_ms * 1e-3) / 1e12
+    x_tflops = mfma_flops / (kern_ms * 1e-3) / 1e12
     alg_gbps = alg_bytes / (kern_ms * 1e-3) / 1e9
     rec = {"bound": "mfma", "achieved": round(k_tflops, 3), "peak": peak, "unit": "TFLOP/s",
            "frac": round(k_tflops / peak, 4), "traffic": traffic,
            "kernel_ms": round(kern_ms, 5),
+           "mfma_executed_flops_per_launch": mfma_flops,
+           "mfma_executed_tflops": round(x_tflops, 3),
+           "mfma_executed_frac": round(x_tflops / peak, 4),
            "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes,
            "hbm_gbps_algorithmic": round(alg_gbps, 2),
            "hbm_frac_algorithmic": round(alg_gbps / PEAK_HBM_GBPS, 4)}
@@ -246,7 +270,8 @@ def other_workloads(dev, steps, warmup):
     for workload, dil in ((2, 1), (2, 8), (2, 512), (2, 2048), (3, None), (4, None)):
         s = setup(workload, dil, "eval", dev)
         ms, kms = timed(s["step"], steps, warmup, dev)
-        rec = roofline(s["flops"], s["alg_bytes"], kms, s["bf16"], measured_traffic(workload))
+        rec = roofline(s["flops"], s["alg_bytes"], kms, s["bf16"], measured_traffic(workload),
+                       s["mfma_flops"])
         rec["kernel"] = s["kernel"]
         res[s["config"]["workload"]] = {
             "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
@@ -372,7 +397,8 @@ def main():
               else f"TFLOP/s & GB/s, {wname}, BN {args.bn}, vs MI355X roofline"
               if "C" in config else f"TFLOP/s & GB/s, {wname}, vs MI355X roofline")
     rl = roofline(flops, alg_bytes, kern_ms_avg, bf16,
-                  measured_traffic(args.workload) if args.bn == "eval" else None)
+                  measured_traffic(args.workload) if args.bn == "eval" else None,
+                  s["mfma_flops"])
     rl["kernel"] = s["kernel"]
 
     line = {

@@ -407,6 +407,14 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
 
 extern "C" {
 
+int dconv1d_block_method(int64_t L, int64_t d) {
+  if (L < 1 || d < 1) return DCONV1D_EINVAL;
+  if (L >= (int64_t(1) << 30)) return DCONV1D_METHOD_DIRECT;
+  const int d_eff = (int)std::min<int64_t>(d, L);
+  return wino_fits((int)L, d_eff) && !winograd_disabled() ? DCONV1D_METHOD_WINOGRAD
+                                                          : DCONV1D_METHOD_DIRECT;
+}
+
 int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* running_var,
                         const float* gamma, const float* beta, float eps, const float* W,
                         const float* b, float* out, int64_t N, int64_t C, int64_t L, int64_t d,

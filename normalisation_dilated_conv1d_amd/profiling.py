@@ -40,6 +40,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = {
     "conv_f32_kernel": ["normalisation_dilated_conv1d_amd/csrc/conv_f32.hip",
                         "normalisation_dilated_conv1d_amd/csrc/internal.h"],
+    "conv_wino_kernel": ["normalisation_dilated_conv1d_amd/csrc/conv_wino.hip",
+                         "normalisation_dilated_conv1d_amd/csrc/internal.h"],
     "conv_bf16_kernel": ["normalisation_dilated_conv1d_amd/csrc/conv_bf16.hip",
                          "normalisation_dilated_conv1d_amd/csrc/internal.h"],
     "conv_gn_fused_kernel": ["normalisation_dilated_conv1d_amd/csrc/conv_gn.hip",

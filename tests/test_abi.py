@@ -14,7 +14,7 @@ EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_noalloc", "prenorm_dconv
             "prenorm_dconv1d_fwd_train_bf16", "relu_dconv1d_residual_fwd",
             "relu_dconv1d_residual_fwd_bf16", "conv1d_groupnorm_fwd",
             "dconv1d_last_error", "dconv1d_release", "dconv1d_timer_enable",
-            "dconv1d_timer_read"}
+            "dconv1d_timer_read", "dconv1d_block_method"}
 
 FAKE_X = 0x10000000
 FAKE_OUT = 0x20000000
@@ -148,3 +148,33 @@ def test_last_error_is_cleared_on_success():
     assert b"C must be" in lib.dconv1d_last_error()
     assert _block(lib, N=0) == dc.DCONV1D_OK
     assert lib.dconv1d_last_error() == b""
+
+
+@pytest.mark.parametrize("L,d,method", [
+    # dilations that divide 32 or are multiples of it take the Winograd form
+    (4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (4096, 1, dc.DCONV1D_METHOD_WINOGRAD),
+    (4096, 8, dc.DCONV1D_METHOD_WINOGRAD), (4096, 2048, dc.DCONV1D_METHOD_WINOGRAD),
+    (4096, 96, dc.DCONV1D_METHOD_WINOGRAD), (4096, 3, dc.DCONV1D_METHOD_DIRECT),
+    (4096, 100, dc.DCONV1D_METHOD_DIRECT), (4096, 48, dc.DCONV1D_METHOD_DIRECT),
+    # d >= L acts as d = L
+    (256, 1000, dc.DCONV1D_METHOD_WINOGRAD), (300, 1000, dc.DCONV1D_METHOD_DIRECT),
+    (1, 7, dc.DCONV1D_METHOD_WINOGRAD),
+    # lengths from 2^28 on keep the direct kernel (32-bit offsets of two rows)
+    ((1 << 28) - 1, 64, dc.DCONV1D_METHOD_WINOGRAD), (1 << 28, 64, dc.DCONV1D_METHOD_DIRECT),
+    ((1 << 30) - 1, 64, dc.DCONV1D_METHOD_DIRECT),
+])
+def test_block_method(L, d, method, monkeypatch):
+    monkeypatch.delenv("DCONV1D_NO_WINOGRAD", raising=False)
+    assert dc.dconv1d_block_method(L, d) == method
+
+
+def test_block_method_switch_and_errors(monkeypatch):
+    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "1")
+    assert dc.dconv1d_block_method(4096, 128) == dc.DCONV1D_METHOD_DIRECT
+    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "0")
+    assert dc.dconv1d_block_method(4096, 128) == dc.DCONV1D_METHOD_WINOGRAD
+    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "")
+    assert dc.dconv1d_block_method(4096, 128) == dc.DCONV1D_METHOD_WINOGRAD
+    lib = dc.load_library()
+    assert lib.dconv1d_block_method(0, 1) == dc.DCONV1D_EINVAL
+    assert lib.dconv1d_block_method(16, 0) == dc.DCONV1D_EINVAL

@@ -1,0 +1,113 @@
+"""The float32 block's two conv forms against the float64 oracle: the Winograd F(2,3)
+kernel (dilations that divide 32 or are multiples of it) and, with DCONV1D_NO_WINOGRAD=1,
+the direct three-tap kernel on the same shapes. Shapes cover both pair-tile layouts (d
+dividing 32: 64 contiguous outputs per tile; d a multiple of 32: two 32-step runs d
+apart), ragged super-blocks, L % 4 != 0 (per-element epilogue), odd chunk counts, two
+output-channel tiles, d >= L, and every entry point that computes the float32 block."""
+import numpy as np
+import pytest
+import torch
+
+import normalisation_dilated_conv1d_amd as dc
+import oracle
+from normalisation_dilated_conv1d_amd.inputs import prenorm_inputs
+
+from test_gpu_parity import TOL_F32, announce, maxrel, oracle_block, run_block, to_dev
+
+pytestmark = pytest.mark.gpu
+
+WINO_CASES = [
+    # (N, C, L, d)
+    (1, 1, 1, 1),
+    (2, 16, 62, 1),          # L % 4 != 0: per-element epilogue; ragged last tile
+    (2, 40, 301, 2),
+    (3, 48, 1000, 4),
+    (2, 33, 257, 16),
+    (2, 64, 100, 32),        # L < 4d: one and a half super-blocks
+    (2, 48, 1000, 96),       # a multiple of 32 that is not a power of two (3 tiles/block)
+    (2, 48, 1000, 160),
+    (2, 300, 700, 64),       # two output-channel tiles, C not a multiple of 32
+    (1, 16, 64, 1000),       # d > L = 64: only the centre tap
+    (4, 96, 2048, 8),        # 3 K-chunks: the loop ends without a barrier
+    (3, 288, 4100, 128),     # 9 K-chunks, two channel tiles, ragged length
+    (2, 32, 4096, 2048),     # d = L/2: one super-block
+]
+
+
+@pytest.fixture
+def direct(monkeypatch):
+    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "1")
+
+
+@pytest.mark.parametrize("N,C,L,d", WINO_CASES)
+def test_winograd_matches_oracle_and_direct(N, C, L, d, monkeypatch):
+    monkeypatch.delenv("DCONV1D_NO_WINOGRAD", raising=False)
+    assert dc.dconv1d_block_method(L, d) == dc.DCONV1D_METHOD_WINOGRAD
+    seed = 50_000 + N * 7 + C * 13 + L + d
+    announce("prenorm_dconv1d_fwd winograd", (N, C, L, d), "seed", seed)
+    p = prenorm_inputs(N, C, L, seed)
+    ref = oracle_block(p, d)
+    wino = run_block(p, d).cpu().numpy()
+    err_w = maxrel(wino, ref)
+    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "1")
+    assert dc.dconv1d_block_method(L, d) == dc.DCONV1D_METHOD_DIRECT
+    direct = run_block(p, d).cpu().numpy()
+    err_d = maxrel(direct, ref)
+    announce(f"   max rel err winograd {err_w:.2e}, direct {err_d:.2e}")
+    assert err_w <= TOL_F32, err_w
+    assert err_d <= TOL_F32, err_d
+
+
+def test_winograd_deterministic_and_grid_invariant():
+    """Two calls give the same bits, and a sample computed alone gives the same bits as
+    inside a batch (the per-output accumulation order does not depend on the grid)."""
+    N, C, L, d = 6, 96, 1024, 64
+    announce("prenorm_dconv1d_fwd winograd bits", (N, C, L, d))
+    p = prenorm_inputs(N, C, L, 61)
+    a = run_block(p, d).cpu()
+    b = run_block(p, d).cpu()
+    assert torch.equal(a, b)
+    one = {k: (v[2:3].contiguous() if k == "x" else v) for k, v in p.items()}
+    alone = run_block(one, d).cpu()
+    assert torch.equal(alone[0], a[2])
+
+
+def test_winograd_negative_infinity_in_last_channel():
+    """-inf at some steps of the last input channel (C not a multiple of 32, so the padded
+    channels read that row): ReLU(BN(-inf)) is 0 with a positive scale, so only the
+    residual itself is non-finite, as in the direct kernel."""
+    N, C, L, d = 2, 40, 300, 4
+    announce("prenorm block winograd -inf in last channel", (N, C, L, d))
+    p = prenorm_inputs(N, C, L, 63)
+    p["gamma"][C - 1] = p["gamma"][C - 1].abs() + 0.5
+    p["x"][:, C - 1, 10:40:3] = float("-inf")
+    got = run_block(p, d).cpu().numpy().astype(np.float64)
+    ref = oracle_block(p, d)
+    bad = ~np.isfinite(ref)
+    assert bad.sum() == N * len(range(10, 40, 3))
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    assert np.all(np.isfinite(got[~bad]))
+    assert maxrel(got[~bad], ref[~bad]) <= TOL_F32
+
+
+def test_winograd_training_mode_and_caller_normalised():
+    """The training-mode and the caller-normalised entry points take the Winograd form
+    too; both against the oracle."""
+    N, C, L, d = 3, 72, 1536, 16
+    announce("prenorm_dconv1d_fwd_train / relu_dconv1d_residual_fwd winograd", (N, C, L, d))
+    p = prenorm_inputs(N, C, L, 64)
+    q = to_dev(p)
+    rm, rv = q["running_mean"].clone(), q["running_var"].clone()
+    got = dc.prenorm_dconv1d_fwd_train(q["x"], rm, rv, q["gamma"], q["beta"], q["eps"], 0.1,
+                                       q["W"], q["b"], d)
+    torch.cuda.synchronize()
+    mean, var = oracle.batch_stats(p["x"])
+    ref = oracle.prenorm_block(p["x"], mean, var, p["gamma"], p["beta"], p["eps"], p["W"],
+                               p["b"], d)
+    assert maxrel(got.cpu().numpy(), ref) <= TOL_F32
+    xn = torch.relu(torch.randn(N, C, L, generator=torch.Generator().manual_seed(65)))
+    res = torch.randn(N, C, L, generator=torch.Generator().manual_seed(66))
+    got = dc.relu_dconv1d_residual_fwd(xn.cuda(), q["W"], q["b"], res.cuda(), d)
+    torch.cuda.synchronize()
+    ref = oracle.relu_conv_residual(xn, p["W"], p["b"], res, d)
+    assert maxrel(got.cpu().numpy(), ref) <= TOL_F32
