@@ -93,9 +93,9 @@ extern "C" {
  * folded once per call in double precision and rounded to float. The conv input is
  * zero-padded after the ReLU, so padded taps contribute exactly 0. Arithmetic:
  * float32 products, float32 accumulation (MFMA), bias and residual added in float32.
- * When min(d, L) divides 32 or is a multiple of 32 (and L < 2^28) the conv runs as
- * Winograd F(2,3) over pairs of outputs d apart: the same sum up to float32 rounding,
- * with 2/3 of the multiply-adds (dconv1d_block_method tells which form a shape takes).
+ * For most dilations the conv runs as Winograd F(2,3) over pairs of outputs d apart:
+ * the same sum up to float32 rounding, with 2/3 of the multiply-adds
+ * (dconv1d_block_method tells which form a shape takes).
  * The float32 entry points below that compute this block (training mode,
  * caller-normalised, no-allocation) choose the same way.
  */
@@ -274,8 +274,9 @@ int dconv1d_timer_read(double* total_ms, int64_t* launches);
 
 /*
  * Which form of the conv a float32 block call of this shape takes (the bf16 entry
- * points always run the direct three-tap kernel): DCONV1D_METHOD_WINOGRAD when
- * min(d, L) divides 32 or is a multiple of 32 and L < 2^28, else DCONV1D_METHOD_DIRECT.
+ * points always run the direct three-tap kernel): DCONV1D_METHOD_WINOGRAD when L < 2^28,
+ * 5*P <= 3*L with P = ceil(L / (2*e)) * e output pairs and e = min(d, L), and e divides
+ * 32, is a multiple of 32 or is at least 16; else DCONV1D_METHOD_DIRECT.
  * Setting the environment variable DCONV1D_NO_WINOGRAD to a value other than "" or "0"
  * (read at every call) makes every float32 block call take the direct form. Returns
  * DCONV1D_EINVAL for L < 1 or d < 1. Host only: no HIP call.

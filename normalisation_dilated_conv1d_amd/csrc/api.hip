@@ -309,9 +309,9 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   // d >= L: both outer taps are always in the padding; d = L gives the same result and
   // keeps every tap offset inside int range.
   const int d_eff = (int)std::min<int64_t>(d, L);
-  // float32 storage takes the Winograd kernel when the dilation divides 32 or is a
-  // multiple of it (32 output pairs and 256 channels per tile), else the direct kernel
-  // with the tile conv_f32_tile picks; bf16 storage runs the bf16-MFMA kernel: 64-channel
+  // float32 storage takes the Winograd kernel when wino_fits says it is faster (not for
+  // d close to L or above it, small irregular d, nor L >= 2^28; 32 output pairs and 256
+  // channels per tile), else the direct kernel with the tile conv_f32_tile picks; bf16 storage runs the bf16-MFMA kernel: 64-channel
   // K-chunks, 128-step time tiles (a 256- or 512-channel tile). The repacked weights are
   // padded to whole channel tiles.
   const bool wino = !bf16 && wino_fits(Li, d_eff) && !winograd_disabled();

@@ -13,11 +13,13 @@
 // and input channel instead of six: the four M_j are four GEMMs of K = C_in, so the
 // kernel runs 2/3 of the direct conv's MFMA work.
 //
-// Pairs. Output step t = 2d*b + r (r < d) pairs with t + d. A tile of 32 pairs is either
-// 32 consecutive r of one super-block b (d a multiple of 32: outputs [T0, T0 + 32) and
-// [T0 + d, T0 + d + 32)) or 32/d whole super-blocks (d dividing 32: outputs
-// [T0, T0 + 64)). With D = min(d, 32), pair c of the tile (0..31) has first step
-//   t0(c) = T0 + 2D*(c / D) + c % D.
+// Pairs. Output step t = 2d*b + r (r < d) pairs with t + d; pair p = d*b + r. A tile is
+// 32 consecutive pairs, so pair c of tile pt has first step t0 = 2d*(p / d) + p % d with
+// p = 32*pt + c. When d is a multiple of 32 the tile is 32 consecutive r of one
+// super-block (outputs [T0, T0 + 32) and [T0 + d, T0 + d + 32)); when d divides 32 it is
+// 32/d whole super-blocks (outputs [T0, T0 + 64)); with D = min(d, 32) both cases read
+//   t0(c) = T0 + 2D*(c / D) + c % D,
+// and the epilogue goes through LDS. Any other dilation takes the per-element epilogue.
 //
 // Work split
 //   workgroup  = one sample n, 256 output channels, 32 pairs (64 output steps); 4 waves,
@@ -58,7 +60,13 @@ constexpr int WMB = 4;                    // 16-channel blocks per wave
 constexpr int WNB = WPAIRS / 16;          // 16-pair blocks per wave
 constexpr int WRPL = KC * WPAIRS / NTHREADS;   // staged (row, pair) items per thread (4)
 
-// first output step of pair tile pt
+// first output step of pair p
+__device__ __forceinline__ int wino_pair_step(int p, int d) {
+  const int b = p / d;
+  return 2 * d * b + (p - b * d);
+}
+
+// first output step of pair tile pt, for a dilation that divides 32 or is a multiple of it
 __device__ __forceinline__ int wino_tile_start(int pt, int d) {
   if (d >= 32) {
     const int per = d >> 5;
@@ -69,8 +77,23 @@ __device__ __forceinline__ int wino_tile_start(int pt, int d) {
 
 }  // namespace
 
+// The Winograd form computes 4 products per output pair and input channel, over every
+// pair of the super-blocks that cover [0, L); the direct form 3 per output step, and it
+// runs its MFMAs at a higher rate (about 0.81 of the peak against 0.67). The Winograd
+// form is taken when the pairs number at most 0.6 L (every dilation up to L/2 that tiles
+// L into whole super-blocks gives L/2; dilations close to L or above it give more, as
+// most pairs' second output then lies past the end), and not for dilations below 16
+// that neither divide 32 nor are multiples of it, whose tiles' outputs fall into many
+// short runs that the per-element epilogue stores slowly (measured on N=32 C=256
+// L=4096: d = 20 to 300 take 374-395 us against 404 us direct, d = 5 409 us, d = 1500
+// 503 us).
 bool wino_fits(int L, int dil) {
-  return L >= 1 && L < (1 << 28) && dil >= 1 && ((dil % 32) == 0 || (32 % dil) == 0);
+  if (L < 1 || L >= (1 << 28) || dil < 1) return false;
+  const long long d = dil < L ? dil : L;
+  const bool regular = (d % 32) == 0 || (32 % d) == 0;
+  if (!regular && d < 16) return false;
+  const long long pairs = ((long long)L + 2 * d - 1) / (2 * d) * d;
+  return 5 * pairs <= 3LL * L;
 }
 
 int wino_pair_tiles(int L, int dil) {
@@ -103,8 +126,10 @@ conv_wino_kernel(ConvF32Args a) {
 
   const int d = a.dil;
   const int L = a.L_in;
-  const int T0 = __builtin_amdgcn_readfirstlane(wino_tile_start(pt, d));
-  const int D = min(d, 32);                 // a power of two
+  // regular: d divides 32 or is a multiple of it (the tile's outputs form one or two runs)
+  const bool regular = (d & 31) == 0 || (32 % d) == 0;
+  const int T0 = __builtin_amdgcn_readfirstlane(regular ? wino_tile_start(pt, d) : 0);
+  const int D = regular ? min(d, 32) : 1;   // a power of two
   const int lgD = __builtin_ctz(D);
 
   const float* __restrict__ xn = reinterpret_cast<const float*>(a.x) + (size_t)n * a.C_in * L;
@@ -126,7 +151,8 @@ conv_wino_kernel(ConvF32Args a) {
   // same for every chunk.
   const int c = l & 31;
   const int hrow = l >> 5;
-  const int t0c = T0 + ((c >> lgD) << (lgD + 1)) + (c & (D - 1));
+  const int t0c = regular ? T0 + ((c >> lgD) << (lgD + 1)) + (c & (D - 1))
+                          : wino_pair_step(WPAIRS * pt + c, d);
   uint32_t toff[4];                         // byte offsets inside a row
   float cap[4];
 #pragma unroll
@@ -245,7 +271,7 @@ conv_wino_kernel(ConvF32Args a) {
   const float* resn = reinterpret_cast<const float*>(a.residual) + (size_t)n * a.C_out * L;
   const int co_w = ct * CO_TILE + 16 * WMB * w;
   const int skip = d > 32 ? d - 32 : 0;
-  const bool vec_epi = ((L & 3) == 0) &&
+  const bool vec_epi = regular && ((L & 3) == 0) &&
                        (((reinterpret_cast<uintptr_t>(a.out) |
                           reinterpret_cast<uintptr_t>(a.residual)) & 15) == 0);
   if (vec_epi) {
@@ -297,26 +323,43 @@ conv_wino_kernel(ConvF32Args a) {
       }
     }
   } else {
+    int ta[WNB];
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) {
+      const int cc = 16 * nb + l16;
+      ta[nb] = regular ? T0 + ((cc >> lgD) << (lgD + 1)) + (cc & (D - 1))
+                       : wino_pair_step(WPAIRS * pt + cc, d);
+    }
+    float rs[WMB][4][WNB][2], bco[WMB][4];
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int coc = min(co_w + 16 * mb + 4 * lq + r, a.C_out - 1);
+        bco[mb][r] = a.bias ? a.bias[coc] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) {
+          rs[mb][r][nb][0] = resn[(size_t)coc * L + min(ta[nb], L - 1)];
+          rs[mb][r][nb][1] = resn[(size_t)coc * L + min(ta[nb] + d, L - 1)];
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int co = co_w + 16 * mb + 4 * lq + r;
-        const int coc = min(co, a.C_out - 1);
-        const float bco = a.bias ? a.bias[coc] : 0.f;
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb) {
-          const int cc = 16 * nb + l16;
-          const int ta = T0 + ((cc >> lgD) << (lgD + 1)) + (cc & (D - 1));
-          const int tb = ta + d;
+          const int tb = ta[nb] + d;
           const float m0 = acc[0][mb][nb][r], m1 = acc[1][mb][nb][r];
           const float m2 = acc[2][mb][nb][r], m3 = acc[3][mb][nb][r];
-          const float ra = resn[(size_t)coc * L + min(ta, L - 1)];
-          const float rb = resn[(size_t)coc * L + min(tb, L - 1)];
-          if (co < a.C_out && ta < L)
-            __builtin_nontemporal_store(((m0 + m1) + m2) + bco + ra, &outn[(size_t)co * L + ta]);
+          if (co < a.C_out && ta[nb] < L)
+            __builtin_nontemporal_store(((m0 + m1) + m2) + bco[mb][r] + rs[mb][r][nb][0],
+                                        &outn[(size_t)co * L + ta[nb]]);
           if (co < a.C_out && tb < L)
-            __builtin_nontemporal_store(((m1 - m2) - m3) + bco + rb, &outn[(size_t)co * L + tb]);
+            __builtin_nontemporal_store(((m1 - m2) - m3) + bco[mb][r] + rs[mb][r][nb][1],
+                                        &outn[(size_t)co * L + tb]);
         }
       }
     }

@@ -151,14 +151,21 @@ def test_last_error_is_cleared_on_success():
 
 
 @pytest.mark.parametrize("L,d,method", [
-    # dilations that divide 32 or are multiples of it take the Winograd form
+    # Winograd when 5 * pairs <= 3 * L, pairs = ceil(L / 2e) * e, e = min(d, L), and e
+    # divides 32, is a multiple of 32 or is at least 16
     (4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (4096, 1, dc.DCONV1D_METHOD_WINOGRAD),
     (4096, 8, dc.DCONV1D_METHOD_WINOGRAD), (4096, 2048, dc.DCONV1D_METHOD_WINOGRAD),
-    (4096, 96, dc.DCONV1D_METHOD_WINOGRAD), (4096, 3, dc.DCONV1D_METHOD_DIRECT),
-    (4096, 100, dc.DCONV1D_METHOD_DIRECT), (4096, 48, dc.DCONV1D_METHOD_DIRECT),
-    # d >= L acts as d = L
-    (256, 1000, dc.DCONV1D_METHOD_WINOGRAD), (300, 1000, dc.DCONV1D_METHOD_DIRECT),
-    (1, 7, dc.DCONV1D_METHOD_WINOGRAD),
+    (4096, 96, dc.DCONV1D_METHOD_WINOGRAD), (4096, 100, dc.DCONV1D_METHOD_WINOGRAD),
+    (4096, 48, dc.DCONV1D_METHOD_WINOGRAD), (4096, 20, dc.DCONV1D_METHOD_WINOGRAD),
+    (4096, 3, dc.DCONV1D_METHOD_DIRECT), (4096, 5, dc.DCONV1D_METHOD_DIRECT),
+    (4096, 15, dc.DCONV1D_METHOD_DIRECT), (4096, 16, dc.DCONV1D_METHOD_WINOGRAD),
+    (4096, 1500, dc.DCONV1D_METHOD_DIRECT),       # pairs 3000: 15000 > 12288
+    (4096, 3000, dc.DCONV1D_METHOD_DIRECT),
+    (7, 2, dc.DCONV1D_METHOD_WINOGRAD),           # pairs 4: 20 <= 21
+    (5, 2, dc.DCONV1D_METHOD_DIRECT),             # pairs 4: 20 > 15
+    # d >= L acts as d = L: every pair's second output lies past the end
+    (256, 1000, dc.DCONV1D_METHOD_DIRECT), (300, 1000, dc.DCONV1D_METHOD_DIRECT),
+    (1, 7, dc.DCONV1D_METHOD_DIRECT), (4096, 4096, dc.DCONV1D_METHOD_DIRECT),
     # lengths from 2^28 on keep the direct kernel (32-bit offsets of two rows)
     ((1 << 28) - 1, 64, dc.DCONV1D_METHOD_WINOGRAD), (1 << 28, 64, dc.DCONV1D_METHOD_DIRECT),
     ((1 << 30) - 1, 64, dc.DCONV1D_METHOD_DIRECT),

@@ -1,9 +1,10 @@
 """The float32 block's two conv forms against the float64 oracle: the Winograd F(2,3)
-kernel (dilations that divide 32 or are multiples of it) and, with DCONV1D_NO_WINOGRAD=1,
-the direct three-tap kernel on the same shapes. Shapes cover both pair-tile layouts (d
-dividing 32: 64 contiguous outputs per tile; d a multiple of 32: two 32-step runs d
-apart), ragged super-blocks, L % 4 != 0 (per-element epilogue), odd chunk counts, two
-output-channel tiles, d >= L, and every entry point that computes the float32 block."""
+kernel and, with DCONV1D_NO_WINOGRAD=1, the direct three-tap kernel on the same shapes.
+Shapes cover both regular pair-tile layouts (d dividing 32: 64 contiguous outputs per
+tile; d a multiple of 32: two 32-step runs d apart), dilations with tiles that cross
+super-blocks, ragged super-blocks, L % 4 != 0 (per-element epilogue), odd chunk counts,
+two output-channel tiles, d near L, and every entry point that computes the float32
+block."""
 import numpy as np
 import pytest
 import torch
@@ -18,25 +19,28 @@ pytestmark = pytest.mark.gpu
 
 WINO_CASES = [
     # (N, C, L, d)
-    (1, 1, 1, 1),
+    (1, 1, 6, 1),
     (2, 16, 62, 1),          # L % 4 != 0: per-element epilogue; ragged last tile
     (2, 40, 301, 2),
     (3, 48, 1000, 4),
     (2, 33, 257, 16),
-    (2, 64, 100, 32),        # L < 4d: one and a half super-blocks
+    (2, 64, 128, 32),        # two super-blocks
     (2, 48, 1000, 96),       # a multiple of 32 that is not a power of two (3 tiles/block)
-    (2, 48, 1000, 160),
+    (2, 48, 1280, 160),
     (2, 300, 700, 64),       # two output-channel tiles, C not a multiple of 32
-    (1, 16, 64, 1000),       # d > L = 64: only the centre tap
     (4, 96, 2048, 8),        # 3 K-chunks: the loop ends without a barrier
     (3, 288, 4100, 128),     # 9 K-chunks, two channel tiles, ragged length
     (2, 32, 4096, 2048),     # d = L/2: one super-block
+    # dilations neither dividing 32 nor multiples of it: tiles cross super-blocks, and the
+    # epilogue is per element
+    (2, 40, 300, 17),
+    (3, 48, 1000, 100),
+    (2, 33, 257, 24),
+    (2, 64, 1000, 127),
+    (3, 288, 4100, 77),
+    (2, 32, 4096, 683),      # three super-blocks
+    (1, 16, 1000, 250),      # two super-blocks
 ]
-
-
-@pytest.fixture
-def direct(monkeypatch):
-    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "1")
 
 
 @pytest.mark.parametrize("N,C,L,d", WINO_CASES)
