@@ -170,7 +170,7 @@ def setup(workload, dilation, bn, dev):
 
         esz = 2 if bf16 else 4
         flops = 2.0 * N * L * C * 3 * C
-        winograd = (not bf16) and dc.dconv1d_block_method(L, d) == dc.DCONV1D_METHOD_WINOGRAD
+        winograd = (not bf16) and dc.dconv1d_block_method(N, C, L, d) == dc.DCONV1D_METHOD_WINOGRAD
         mfma_flops = winograd_mfma_flops(N, C, L, d) if winograd else flops
         alg_bytes = esz * 2.0 * N * C * L + 4.0 * (3 * C * C + 5 * C)
         if bn != "eval":

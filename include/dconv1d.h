@@ -273,17 +273,21 @@ int dconv1d_timer_enable(int enable);
 int dconv1d_timer_read(double* total_ms, int64_t* launches);
 
 /*
- * Which form of the conv a float32 block call of this shape takes (the bf16 entry
- * points always run the direct three-tap kernel): DCONV1D_METHOD_WINOGRAD when L < 2^28,
- * 5*P <= 3*L with P = ceil(L / (2*e)) * e output pairs and e = min(d, L), and e divides
- * 32, is a multiple of 32 or is at least 16; else DCONV1D_METHOD_DIRECT.
- * Setting the environment variable DCONV1D_NO_WINOGRAD to a value other than "" or "0"
- * (read at every call) makes every float32 block call take the direct form. Returns
- * DCONV1D_EINVAL for L < 1 or d < 1. Host only: no HIP call.
+ * Which form of the conv a float32 block call of this shape (N, C, L, d) takes (the bf16
+ * entry points always run the direct three-tap kernel). By default
+ * DCONV1D_METHOD_WINOGRAD when L < 2^28; 5*P <= 3*L with P = ceil(L / (2*e)) * e output
+ * pairs and e = min(d, L); e divides 32, is a multiple of 32 or is at least 16; and
+ * N * ceil(P / 32) * ceil(C / 256) >= 256 (a workgroup per compute unit); else
+ * DCONV1D_METHOD_DIRECT. The environment variable DCONV1D_WINOGRAD, read at every call,
+ * overrides this: "0" selects the direct form always, "1" the Winograd form for every
+ * L < 2^28. Returns DCONV1D_EINVAL for N < 0, C outside [1, 16384], L < 1 or d < 1.
+ * Host only: no HIP call. Each form gives a sample the same bits at any N; as the
+ * automatic choice depends on N, a sample's result may differ in its last bits between
+ * batch sizes on either side of it (both within float32 rounding of the exact sum).
  */
 #define DCONV1D_METHOD_DIRECT 0
 #define DCONV1D_METHOD_WINOGRAD 1
-int dconv1d_block_method(int64_t L, int64_t d);
+int dconv1d_block_method(int64_t N, int64_t C, int64_t L, int64_t d);
 
 #ifdef __cplusplus
 }

@@ -70,7 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dconv1d_timer_enable.restype = ctypes.c_int
     lib.dconv1d_timer_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.dconv1d_timer_read.restype = ctypes.c_int
-    lib.dconv1d_block_method.argtypes = [I64, I64]
+    lib.dconv1d_block_method.argtypes = [I64, I64, I64, I64]
     lib.dconv1d_block_method.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -287,10 +287,10 @@ DCONV1D_METHOD_DIRECT = 0
 DCONV1D_METHOD_WINOGRAD = 1
 
 
-def dconv1d_block_method(L: int, d: int) -> int:
-    """Which form of the conv a float32 block call with length L and dilation d takes:
-    DCONV1D_METHOD_WINOGRAD or DCONV1D_METHOD_DIRECT (host only, no GPU needed)."""
-    code = load_library().dconv1d_block_method(int(L), int(d))
+def dconv1d_block_method(N: int, C: int, L: int, d: int) -> int:
+    """Which form of the conv a float32 block call of shape (N, C, L) and dilation d
+    takes: DCONV1D_METHOD_WINOGRAD or DCONV1D_METHOD_DIRECT (host only, no GPU needed)."""
+    code = load_library().dconv1d_block_method(int(N), int(C), int(L), int(d))
     if code < 0:
         _check(code)
     return code

@@ -204,11 +204,15 @@ void timer_end(int slot, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- algorithm choice
-// DCONV1D_NO_WINOGRAD=1 in the environment (read at every call) makes the float32 block
-// use the direct three-tap kernel for every dilation, e.g. to compare the two.
-bool winograd_disabled() {
-  const char* v = std::getenv("DCONV1D_NO_WINOGRAD");
-  return v != nullptr && v[0] != '\0' && v[0] != '0';
+// The float32 block's conv form: Winograd when the kernel can run the shape and is the
+// faster one. DCONV1D_WINOGRAD in the environment (read at every call) overrides that:
+// "0" the direct kernel always, "1" the Winograd kernel whenever it can run the shape
+// (e.g. to compare the two, or to test the Winograd kernel on small shapes).
+bool use_winograd(int64_t N, int C, int L, int d_eff) {
+  const char* v = std::getenv("DCONV1D_WINOGRAD");
+  if (v != nullptr && v[0] == '0' && v[1] == '\0') return false;
+  if (v != nullptr && v[0] == '1' && v[1] == '\0') return wino_supported(L);
+  return wino_faster((long long)N, C, L, d_eff);
 }
 
 // ---------------------------------------------------------------- shared checks
@@ -309,12 +313,11 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   // d >= L: both outer taps are always in the padding; d = L gives the same result and
   // keeps every tap offset inside int range.
   const int d_eff = (int)std::min<int64_t>(d, L);
-  // float32 storage takes the Winograd kernel when wino_fits says it is faster (not for
-  // d close to L or above it, small irregular d, nor L >= 2^28; 32 output pairs and 256
-  // channels per tile), else the direct kernel with the tile conv_f32_tile picks; bf16 storage runs the bf16-MFMA kernel: 64-channel
+  // float32 storage takes the Winograd kernel when use_winograd says so (32 output pairs
+  // and 256 channels per tile), else the direct kernel with the tile conv_f32_tile picks; bf16 storage runs the bf16-MFMA kernel: 64-channel
   // K-chunks, 128-step time tiles (a 256- or 512-channel tile). The repacked weights are
   // padded to whole channel tiles.
-  const bool wino = !bf16 && wino_fits(Li, d_eff) && !winograd_disabled();
+  const bool wino = !bf16 && use_winograd(N, Ci, Li, d_eff);
   const int Cin_pad = round_up(Ci, bf16 ? CIN_PAD_BF16 : KC);
   const int co_tile_bf16 = bf16 ? conv_bf16_co_tile(N, Li, Ci) : 0;
   const int Cout_pad = round_up(Ci, bf16 ? co_tile_bf16 : CO_TILE_F32);
@@ -407,12 +410,12 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
 
 extern "C" {
 
-int dconv1d_block_method(int64_t L, int64_t d) {
-  if (L < 1 || d < 1) return DCONV1D_EINVAL;
-  if (L >= (int64_t(1) << 30)) return DCONV1D_METHOD_DIRECT;
+int dconv1d_block_method(int64_t N, int64_t C, int64_t L, int64_t d) {
+  if (N < 0 || C < 1 || C > kMaxChannels || L < 1 || d < 1) return DCONV1D_EINVAL;
+  if (L >= (int64_t(1) << 30) || N == 0) return DCONV1D_METHOD_DIRECT;
   const int d_eff = (int)std::min<int64_t>(d, L);
-  return wino_fits((int)L, d_eff) && !winograd_disabled() ? DCONV1D_METHOD_WINOGRAD
-                                                          : DCONV1D_METHOD_DIRECT;
+  return use_winograd(N, (int)C, (int)L, d_eff) ? DCONV1D_METHOD_WINOGRAD
+                                                : DCONV1D_METHOD_DIRECT;
 }
 
 int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* running_var,

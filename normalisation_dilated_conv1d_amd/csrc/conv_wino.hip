@@ -77,23 +77,30 @@ __device__ __forceinline__ int wino_tile_start(int pt, int d) {
 
 }  // namespace
 
-// The Winograd form computes 4 products per output pair and input channel, over every
-// pair of the super-blocks that cover [0, L); the direct form 3 per output step, and it
-// runs its MFMAs at a higher rate (about 0.81 of the peak against 0.67). The Winograd
-// form is taken when the pairs number at most 0.6 L (every dilation up to L/2 that tiles
-// L into whole super-blocks gives L/2; dilations close to L or above it give more, as
-// most pairs' second output then lies past the end), and not for dilations below 16
-// that neither divide 32 nor are multiples of it, whose tiles' outputs fall into many
-// short runs that the per-element epilogue stores slowly (measured on N=32 C=256
-// L=4096: d = 20 to 300 take 374-395 us against 404 us direct, d = 5 409 us, d = 1500
-// 503 us).
-bool wino_fits(int L, int dil) {
-  if (L < 1 || L >= (1 << 28) || dil < 1) return false;
+// The kernel runs any dilation; two rows' byte offsets must fit 32 bits.
+bool wino_supported(int L) { return L >= 1 && L < (1 << 28); }
+
+// Whether the Winograd form is the faster one. It computes 4 products per output pair
+// and input channel, over every pair of the super-blocks that cover [0, L); the direct
+// form 3 per output step, and it runs its MFMAs at a higher rate (about 0.81 of the peak
+// against 0.67). So the Winograd form needs at most 0.6 L pairs (every dilation up to
+// L/2 that tiles L into whole super-blocks gives L/2; dilations close to L or above it
+// give more, as most pairs' second output then lies past the end); not a dilation below
+// 16 that neither divides 32 nor is a multiple of it, whose tiles' outputs fall into many
+// short runs that the per-element epilogue stores slowly; and at least one workgroup per
+// CU (256), below which the direct kernel's smaller tiles fill the chip better. Measured
+// on C=256 L=4096 against the direct kernel: N=32, d = 20 to 300: 374-395 us against
+// 404 us, d = 5: 409 us, d = 1500: 503 us; d = 128, N = 1 and 2: 43 us against 37-38 us,
+// N = 4: 45 us against 66 us.
+bool wino_faster(long long N, int C, int L, int dil) {
+  if (!wino_supported(L) || dil < 1 || N < 1 || C < 1) return false;
   const long long d = dil < L ? dil : L;
   const bool regular = (d % 32) == 0 || (32 % d) == 0;
   if (!regular && d < 16) return false;
   const long long pairs = ((long long)L + 2 * d - 1) / (2 * d) * d;
-  return 5 * pairs <= 3LL * L;
+  if (5 * pairs > 3LL * L) return false;
+  const long long wgs = N * ((pairs + WPAIRS - 1) / WPAIRS) * ((C + 64 * WMB - 1) / (64 * WMB));
+  return wgs >= 256;
 }
 
 int wino_pair_tiles(int L, int dil) {
@@ -371,7 +378,8 @@ hipError_t launch_conv_wino(const ConvF32Args& a, hipStream_t stream) {
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.scale == nullptr || a.C_in != a.C_out || a.L_in != a.L_out || a.pad != a.dil ||
-      !wino_fits(a.L_in, a.dil) || a.n_tt != wino_pair_tiles(a.L_in, a.dil) ||
+      !wino_supported(a.L_in) || a.dil < 1 || a.dil > a.L_in ||
+      a.n_tt != wino_pair_tiles(a.L_in, a.dil) ||
       a.NCB * 16 < a.n_ct * 64 * WMB || a.Q * KC < a.C_in)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(conv_wino_kernel, dim3((unsigned)nwg), dim3(NTHREADS), 0, stream, a);

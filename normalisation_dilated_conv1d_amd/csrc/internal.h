@@ -67,10 +67,12 @@ hipError_t launch_prep_wino(const float* W, int C_out, int C_in, int Cout_pad, i
                             float* Up, const float* running_mean, const float* running_var,
                             const float* gamma, const float* beta, float eps, float* scale,
                             float* shift, hipStream_t stream);
-// conv_wino.hip: the float32 block by Winograd F(2,3) along the dilation lattice, when
-// wino_fits(L, d) (L_in < 2^28 and faster than the direct form); 32 output pairs per
-// workgroup, a.n_tt = wino_pair_tiles(L, d), a.Q = Cin_pad / KC
-bool wino_fits(int L, int dil);
+// conv_wino.hip: the float32 block by Winograd F(2,3) along the dilation lattice, for
+// wino_supported(L) (L_in < 2^28), taken by default when wino_faster(N, C, L, d); 32
+// output pairs per workgroup, a.n_tt = wino_pair_tiles(L, d), a.Q = Cin_pad / KC, a.dil
+// = a.pad = min(d, L)
+bool wino_supported(int L);
+bool wino_faster(long long N, int C, int L, int dil);
 int wino_pair_tiles(int L, int dil);
 hipError_t launch_conv_wino(const ConvF32Args& a, hipStream_t stream);
 

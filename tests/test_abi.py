@@ -150,38 +150,49 @@ def test_last_error_is_cleared_on_success():
     assert lib.dconv1d_last_error() == b""
 
 
-@pytest.mark.parametrize("L,d,method", [
-    # Winograd when 5 * pairs <= 3 * L, pairs = ceil(L / 2e) * e, e = min(d, L), and e
-    # divides 32, is a multiple of 32 or is at least 16
-    (4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (4096, 1, dc.DCONV1D_METHOD_WINOGRAD),
-    (4096, 8, dc.DCONV1D_METHOD_WINOGRAD), (4096, 2048, dc.DCONV1D_METHOD_WINOGRAD),
-    (4096, 96, dc.DCONV1D_METHOD_WINOGRAD), (4096, 100, dc.DCONV1D_METHOD_WINOGRAD),
-    (4096, 48, dc.DCONV1D_METHOD_WINOGRAD), (4096, 20, dc.DCONV1D_METHOD_WINOGRAD),
-    (4096, 3, dc.DCONV1D_METHOD_DIRECT), (4096, 5, dc.DCONV1D_METHOD_DIRECT),
-    (4096, 15, dc.DCONV1D_METHOD_DIRECT), (4096, 16, dc.DCONV1D_METHOD_WINOGRAD),
-    (4096, 1500, dc.DCONV1D_METHOD_DIRECT),       # pairs 3000: 15000 > 12288
-    (4096, 3000, dc.DCONV1D_METHOD_DIRECT),
-    (7, 2, dc.DCONV1D_METHOD_WINOGRAD),           # pairs 4: 20 <= 21
-    (5, 2, dc.DCONV1D_METHOD_DIRECT),             # pairs 4: 20 > 15
+@pytest.mark.parametrize("N,C,L,d,method", [
+    # Winograd when 5 * pairs <= 3 * L, pairs = ceil(L / 2e) * e, e = min(d, L); e divides
+    # 32, is a multiple of 32 or is at least 16; and at least 256 workgroups
+    (32, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 1, dc.DCONV1D_METHOD_WINOGRAD),
+    (32, 256, 4096, 8, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 2048, dc.DCONV1D_METHOD_WINOGRAD),
+    (32, 256, 4096, 96, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 100, dc.DCONV1D_METHOD_WINOGRAD),
+    (32, 256, 4096, 48, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 20, dc.DCONV1D_METHOD_WINOGRAD),
+    (32, 256, 4096, 3, dc.DCONV1D_METHOD_DIRECT), (32, 256, 4096, 5, dc.DCONV1D_METHOD_DIRECT),
+    (32, 256, 4096, 15, dc.DCONV1D_METHOD_DIRECT), (32, 256, 4096, 16, dc.DCONV1D_METHOD_WINOGRAD),
+    (32, 256, 4096, 1500, dc.DCONV1D_METHOD_DIRECT),   # pairs 3000: 15000 > 12288
+    (32, 256, 4096, 3000, dc.DCONV1D_METHOD_DIRECT),
+    (512, 16, 7, 2, dc.DCONV1D_METHOD_WINOGRAD),       # pairs 4: 20 <= 21
+    (512, 16, 5, 2, dc.DCONV1D_METHOD_DIRECT),         # pairs 4: 20 > 15
     # d >= L acts as d = L: every pair's second output lies past the end
-    (256, 1000, dc.DCONV1D_METHOD_DIRECT), (300, 1000, dc.DCONV1D_METHOD_DIRECT),
-    (1, 7, dc.DCONV1D_METHOD_DIRECT), (4096, 4096, dc.DCONV1D_METHOD_DIRECT),
+    (512, 16, 256, 1000, dc.DCONV1D_METHOD_DIRECT), (512, 16, 1, 7, dc.DCONV1D_METHOD_DIRECT),
+    (32, 256, 4096, 4096, dc.DCONV1D_METHOD_DIRECT),
+    # fewer workgroups than compute units: 64 pair tiles per sample at L = 4096, d = 128
+    (1, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT), (3, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
+    (4, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 512, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
+    (0, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
     # lengths from 2^28 on keep the direct kernel (32-bit offsets of two rows)
-    ((1 << 28) - 1, 64, dc.DCONV1D_METHOD_WINOGRAD), (1 << 28, 64, dc.DCONV1D_METHOD_DIRECT),
-    ((1 << 30) - 1, 64, dc.DCONV1D_METHOD_DIRECT),
+    (1, 1, (1 << 28) - 1, 64, dc.DCONV1D_METHOD_WINOGRAD), (1, 1, 1 << 28, 64, dc.DCONV1D_METHOD_DIRECT),
+    (1, 1, (1 << 30) - 1, 64, dc.DCONV1D_METHOD_DIRECT),
 ])
-def test_block_method(L, d, method, monkeypatch):
-    monkeypatch.delenv("DCONV1D_NO_WINOGRAD", raising=False)
-    assert dc.dconv1d_block_method(L, d) == method
+def test_block_method(N, C, L, d, method, monkeypatch):
+    monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
+    assert dc.dconv1d_block_method(N, C, L, d) == method
 
 
 def test_block_method_switch_and_errors(monkeypatch):
-    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "1")
-    assert dc.dconv1d_block_method(4096, 128) == dc.DCONV1D_METHOD_DIRECT
-    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "0")
-    assert dc.dconv1d_block_method(4096, 128) == dc.DCONV1D_METHOD_WINOGRAD
-    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "")
-    assert dc.dconv1d_block_method(4096, 128) == dc.DCONV1D_METHOD_WINOGRAD
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "0")
+    assert dc.dconv1d_block_method(32, 256, 4096, 128) == dc.DCONV1D_METHOD_DIRECT
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
+    assert dc.dconv1d_block_method(1, 16, 62, 1) == dc.DCONV1D_METHOD_WINOGRAD
+    assert dc.dconv1d_block_method(1, 16, 62, 1000) == dc.DCONV1D_METHOD_WINOGRAD
+    assert dc.dconv1d_block_method(1, 16, 1 << 28, 1) == dc.DCONV1D_METHOD_DIRECT
+    for v in ("", "2", "yes"):    # anything else: the automatic choice
+        monkeypatch.setenv("DCONV1D_WINOGRAD", v)
+        assert dc.dconv1d_block_method(1, 16, 62, 1) == dc.DCONV1D_METHOD_DIRECT
+        assert dc.dconv1d_block_method(32, 256, 4096, 128) == dc.DCONV1D_METHOD_WINOGRAD
     lib = dc.load_library()
-    assert lib.dconv1d_block_method(0, 1) == dc.DCONV1D_EINVAL
-    assert lib.dconv1d_block_method(16, 0) == dc.DCONV1D_EINVAL
+    assert lib.dconv1d_block_method(-1, 16, 16, 1) == dc.DCONV1D_EINVAL
+    assert lib.dconv1d_block_method(1, 0, 16, 1) == dc.DCONV1D_EINVAL
+    assert lib.dconv1d_block_method(1, 16385, 16, 1) == dc.DCONV1D_EINVAL
+    assert lib.dconv1d_block_method(1, 16, 0, 1) == dc.DCONV1D_EINVAL
+    assert lib.dconv1d_block_method(1, 16, 16, 0) == dc.DCONV1D_EINVAL

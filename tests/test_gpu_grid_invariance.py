@@ -1,8 +1,9 @@
 """Results must not depend on how many workgroups a launch has: the same samples computed
 alone and inside larger batches give bitwise-equal outputs. The batch sizes are chosen so
 that the library picks a different tile (and so a different grid and workgroup shape) for
-each: for the float32 block at C=256, L=4096 the 64x128 tile below N=8, the 64x256 tile
-for 8 <= N < 16 and the 128x256 tile from N=16; for the bf16 block at C=512, L=16384 the
+each: for the float32 block's direct kernel at C=256, L=4096 the 64x128 tile below N=8, the
+64x256 tile for 8 <= N < 16 and the 128x256 tile from N=16 (and the Winograd kernel's grid
+at each N); for the bf16 block at C=512, L=16384 the
 256-channel tile at N=1 and the 512-channel tile from N=2; and for Conv1d+GroupNorm the
 single-launch kernel at 16 and at 640 workgroups. Every output is a fixed sequence of MFMA
 steps over the same K order whatever the tile, so equal bits are the bar. A missing
@@ -26,9 +27,15 @@ def _block(q, n0, n1, d, bf16=False):
               q["b"], d)
 
 
-def test_f32_block_same_bits_for_every_tile():
+@pytest.mark.parametrize("form", ["0", "1"])
+def test_f32_block_same_bits_for_every_tile(form, monkeypatch):
+    """Each conv form on its own (DCONV1D_WINOGRAD=0: the direct kernel, whose tile changes
+    with N; =1: the Winograd kernel, whose grid changes with N). Without the override the
+    library picks the form by shape, N included, so a sample's bits may differ between
+    batch sizes that fall on either side of that choice."""
+    monkeypatch.setenv("DCONV1D_WINOGRAD", form)
     N, C, L, d = 20, 256, 4096, 128
-    announce("grid invariance f32", (N, C, L, d))
+    announce("grid invariance f32", (N, C, L, d), "DCONV1D_WINOGRAD", form)
     q = to_dev(prenorm_inputs(N, C, L, 90_001))
     full = _block(q, 0, N, d)                 # 128 x 256 tiles, 640 workgroups
     mid = _block(q, 2, 12, d)                 # N = 10: 64 x 256 tiles

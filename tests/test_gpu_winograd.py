@@ -1,5 +1,6 @@
 """The float32 block's two conv forms against the float64 oracle: the Winograd F(2,3)
-kernel and, with DCONV1D_NO_WINOGRAD=1, the direct three-tap kernel on the same shapes.
+kernel (DCONV1D_WINOGRAD=1: these shapes are too small for the automatic choice to take
+it) and, with DCONV1D_WINOGRAD=0, the direct three-tap kernel on the same shapes.
 Shapes cover both regular pair-tile layouts (d dividing 32: 64 contiguous outputs per
 tile; d a multiple of 32: two 32-step runs d apart), dilations with tiles that cross
 super-blocks, ragged super-blocks, L % 4 != 0 (per-element epilogue), odd chunk counts,
@@ -45,16 +46,16 @@ WINO_CASES = [
 
 @pytest.mark.parametrize("N,C,L,d", WINO_CASES)
 def test_winograd_matches_oracle_and_direct(N, C, L, d, monkeypatch):
-    monkeypatch.delenv("DCONV1D_NO_WINOGRAD", raising=False)
-    assert dc.dconv1d_block_method(L, d) == dc.DCONV1D_METHOD_WINOGRAD
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
+    assert dc.dconv1d_block_method(N, C, L, d) == dc.DCONV1D_METHOD_WINOGRAD
     seed = 50_000 + N * 7 + C * 13 + L + d
     announce("prenorm_dconv1d_fwd winograd", (N, C, L, d), "seed", seed)
     p = prenorm_inputs(N, C, L, seed)
     ref = oracle_block(p, d)
     wino = run_block(p, d).cpu().numpy()
     err_w = maxrel(wino, ref)
-    monkeypatch.setenv("DCONV1D_NO_WINOGRAD", "1")
-    assert dc.dconv1d_block_method(L, d) == dc.DCONV1D_METHOD_DIRECT
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "0")
+    assert dc.dconv1d_block_method(N, C, L, d) == dc.DCONV1D_METHOD_DIRECT
     direct = run_block(p, d).cpu().numpy()
     err_d = maxrel(direct, ref)
     announce(f"   max rel err winograd {err_w:.2e}, direct {err_d:.2e}")
@@ -62,9 +63,10 @@ def test_winograd_matches_oracle_and_direct(N, C, L, d, monkeypatch):
     assert err_d <= TOL_F32, err_d
 
 
-def test_winograd_deterministic_and_grid_invariant():
+def test_winograd_deterministic_and_grid_invariant(monkeypatch):
     """Two calls give the same bits, and a sample computed alone gives the same bits as
     inside a batch (the per-output accumulation order does not depend on the grid)."""
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
     N, C, L, d = 6, 96, 1024, 64
     announce("prenorm_dconv1d_fwd winograd bits", (N, C, L, d))
     p = prenorm_inputs(N, C, L, 61)
@@ -76,10 +78,11 @@ def test_winograd_deterministic_and_grid_invariant():
     assert torch.equal(alone[0], a[2])
 
 
-def test_winograd_negative_infinity_in_last_channel():
+def test_winograd_negative_infinity_in_last_channel(monkeypatch):
     """-inf at some steps of the last input channel (C not a multiple of 32, so the padded
     channels read that row): ReLU(BN(-inf)) is 0 with a positive scale, so only the
     residual itself is non-finite, as in the direct kernel."""
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
     N, C, L, d = 2, 40, 300, 4
     announce("prenorm block winograd -inf in last channel", (N, C, L, d))
     p = prenorm_inputs(N, C, L, 63)
@@ -94,9 +97,10 @@ def test_winograd_negative_infinity_in_last_channel():
     assert maxrel(got[~bad], ref[~bad]) <= TOL_F32
 
 
-def test_winograd_training_mode_and_caller_normalised():
+def test_winograd_training_mode_and_caller_normalised(monkeypatch):
     """The training-mode and the caller-normalised entry points take the Winograd form
     too; both against the oracle."""
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
     N, C, L, d = 3, 72, 1536, 16
     announce("prenorm_dconv1d_fwd_train / relu_dconv1d_residual_fwd winograd", (N, C, L, d))
     p = prenorm_inputs(N, C, L, 64)
@@ -115,3 +119,15 @@ def test_winograd_training_mode_and_caller_normalised():
     torch.cuda.synchronize()
     ref = oracle.relu_conv_residual(xn, p["W"], p["b"], res, d)
     assert maxrel(got.cpu().numpy(), ref) <= TOL_F32
+
+
+def test_automatic_choice_on_a_full_grid(monkeypatch):
+    """Without the override, a shape with a workgroup per compute unit takes the Winograd
+    form and one with fewer the direct form; both against the oracle."""
+    monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
+    for N, C, L, d, method in ((4, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
+                               (1, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT)):
+        assert dc.dconv1d_block_method(N, C, L, d) == method
+        announce("prenorm_dconv1d_fwd automatic", (N, C, L, d), "method", method)
+        p = prenorm_inputs(N, C, L, 67 + N)
+        assert maxrel(run_block(p, d).cpu().numpy(), oracle_block(p, d)) <= TOL_F32
