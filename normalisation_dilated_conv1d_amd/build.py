@@ -26,13 +26,13 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
 
-# Flags for one source only. The fp32 conv kernels run about 1% faster when the AMDGPU
-# machine scheduler favours instruction-level parallelism over register pressure (the
-# same registers, the same MFMA order per accumulator, so bitwise the same output); the
-# bf16 kernel runs about 1% slower that way, so the choice is per file.
+# Flags for one source only. The direct fp32 conv kernel runs about 1% faster when the
+# AMDGPU machine scheduler favours instruction-level parallelism over register pressure
+# (the same registers, the same MFMA order per accumulator, so bitwise the same output);
+# the bf16 kernel runs about 1% slower that way, and the Winograd kernel spills with it
+# for no gain, so the choice is per file.
 FILE_FLAGS = {
     "conv_f32.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-    "conv_wino.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 

@@ -36,7 +36,11 @@
 //                64*(c/16) + 4*(c%16) + j, so a lane's B values of one MFMA step (pairs
 //                l%16 and 16 + l%16, all four j) are two 16-byte LDS reads.
 //   A operand  = U_j from the repack of prep_wino_kernel, one 16-byte load per (step,
-//                16-channel block) holding the four j, one step ahead.
+//                16-channel block) holding the four j, two steps ahead: the MFMAs of a
+//                step run block by block, and each block's register slot is refilled for
+//                the step after next as soon as its MFMAs have issued. One step ahead was
+//                too short for a workgroup alone on its CU (its step takes half as long
+//                as with a partner): 9% slower overall.
 //   Epilogue   = y(t0), y(t0 + d) from the four accumulator sets in registers, then as in
 //                the direct kernel: through LDS so that a lane owns 4 consecutive steps,
 //                + bias + residual (16-byte loads), non-temporal 16-byte stores.
@@ -209,6 +213,10 @@ conv_wino_kernel(ConvF32Args a) {
   };
   // A operands of MFMA step s of chunk q: one float4 (U0..U3) per 16-channel block
   const int Q = a.Q;
+  auto load_a1 = [&](int q, int s, int mb, f32x4& dst) {
+    q = min(q, Q - 1);
+    dst = Up4[(size_t)((8 * q + s) * a.NCB + cb0 + mb) * 64 + l];
+  };
   auto load_a = [&](int q, int s, f32x4 (&dst)[WMB]) {
     q = min(q, Q - 1);
 #pragma unroll
@@ -231,18 +239,19 @@ conv_wino_kernel(ConvF32Args a) {
     load_b(zb, 0, bv[0]);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      // the next step's operands (the next chunk's first A at the last step) go out first
-      load_a(s + 1 < 8 ? q : q + 1, (s + 1) & 7, au[(s + 1) & 1]);
       if (s + 1 < 8) load_b(zb, s + 1, bv[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int mb = 0; mb < WMB; ++mb) {
 #pragma unroll
-        for (int mb = 0; mb < WMB; ++mb)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int nb = 0; nb < WNB; ++nb)
             acc[j][mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                 au[s & 1][mb][j], bv[s & 1][nb][j], acc[j][mb][nb], 0, 0, 0);
+        // the block's slot now holds what step s + 2 needs
+        load_a1(s + 2 < 8 ? q : q + 1, (s + 2) & 7, mb, au[s & 1][mb]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (s == 3) {
         mid();
@@ -252,6 +261,7 @@ conv_wino_kernel(ConvF32Args a) {
   };
 
   load_a(0, 0, au[0]);
+  load_a(0, 1, au[1]);
   load_x(0);
   store_z(zs0);
   __syncthreads();
