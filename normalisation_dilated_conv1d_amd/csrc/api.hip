@@ -203,7 +203,45 @@ void timer_end(int slot, hipStream_t s) {
   (void)hipEventRecord(g_timer.ev[2 * slot + 1], s);
 }
 
+}  // namespace
+
 // ---------------------------------------------------------------- algorithm choice
+namespace dconv1d {
+
+// The kernel runs any dilation; two rows' byte offsets must fit 32 bits.
+bool wino_supported(int L) { return L >= 1 && L < (1 << 28); }
+
+// Whether the Winograd form is the faster one. It computes 4 products per output pair
+// and input channel, over every pair of the super-blocks that cover [0, L); the direct
+// form 3 per output step, and it runs its MFMAs at a higher rate (about 0.81 of the peak
+// against 0.74). So the Winograd form needs at most 2L/3 pairs (every dilation up to L/2
+// that tiles L into whole super-blocks gives L/2; dilations close to L or above it give
+// more, as most pairs' second output then lies past the end), and a grid of at least 160
+// workgroups (5/8 of the CUs), below which the direct kernel's smaller tiles fill the
+// chip better. Measured on C=256 L=4096 against the direct kernel's 404 us at N=32:
+// d = 3 to 300 348-373 us, d = 2500 (P = 0.61 L) 382 us, d = 1500 (P = 0.73 L) 453 us;
+// at d = 128: N = 1 and 2 (64 and 128 workgroups) 44 us against 38-39 us, N = 3 (192)
+// 45 us against 65 us.
+bool wino_faster(long long N, int C, int L, int dil) {
+  if (!wino_supported(L) || dil < 1 || N < 1 || C < 1) return false;
+  const long long d = dil < L ? dil : L;
+  const long long pairs = ((long long)L + 2 * d - 1) / (2 * d) * d;
+  if (3 * pairs > 2LL * L) return false;
+  const long long wgs =
+      N * ((pairs + WINO_PAIRS - 1) / WINO_PAIRS) * ((C + WINO_CO_TILE - 1) / WINO_CO_TILE);
+  return wgs >= 160;
+}
+
+int wino_pair_tiles(int L, int dil) {
+  const long long blocks = ((long long)L + 2LL * dil - 1) / (2LL * dil);   // super-blocks
+  const long long pairs = blocks * dil;
+  return (int)((pairs + WINO_PAIRS - 1) / WINO_PAIRS);
+}
+
+}  // namespace dconv1d
+
+namespace {
+
 // The float32 block's conv form: Winograd when the kernel can run the shape and is the
 // faster one. DCONV1D_WINOGRAD in the environment (read at every call) overrides that:
 // "0" the direct kernel always, "1" the Winograd kernel whenever it can run the shape

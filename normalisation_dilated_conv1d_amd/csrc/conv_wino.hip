@@ -57,10 +57,10 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int WPAIRS = 32;                // output pairs per workgroup
+constexpr int WPAIRS = WINO_PAIRS;        // output pairs per workgroup
 constexpr int WPITCH = 4 * WPAIRS + 4;    // floats per staged row (four V_j per pair)
 constexpr int WEP = 2 * WPAIRS + 4;       // floats per epilogue row (64 output steps)
-constexpr int WMB = 4;                    // 16-channel blocks per wave
+constexpr int WMB = WINO_CO_TILE / 64;    // 16-channel blocks per wave
 constexpr int WNB = WPAIRS / 16;          // 16-pair blocks per wave
 constexpr int WRPL = KC * WPAIRS / NTHREADS;   // staged (row, pair) items per thread (4)
 
@@ -80,38 +80,6 @@ __device__ __forceinline__ int wino_tile_start(int pt, int d) {
 }
 
 }  // namespace
-
-// The kernel runs any dilation; two rows' byte offsets must fit 32 bits.
-bool wino_supported(int L) { return L >= 1 && L < (1 << 28); }
-
-// Whether the Winograd form is the faster one. It computes 4 products per output pair
-// and input channel, over every pair of the super-blocks that cover [0, L); the direct
-// form 3 per output step, and it runs its MFMAs at a higher rate (about 0.81 of the peak
-// against 0.67). So the Winograd form needs at most 0.6 L pairs (every dilation up to
-// L/2 that tiles L into whole super-blocks gives L/2; dilations close to L or above it
-// give more, as most pairs' second output then lies past the end); not a dilation below
-// 16 that neither divides 32 nor is a multiple of it, whose tiles' outputs fall into many
-// short runs that the per-element epilogue stores slowly; and at least one workgroup per
-// CU (256), below which the direct kernel's smaller tiles fill the chip better. Measured
-// on C=256 L=4096 against the direct kernel: N=32, d = 20 to 300: 374-395 us against
-// 404 us, d = 5: 409 us, d = 1500: 503 us; d = 128, N = 1 and 2: 43 us against 37-38 us,
-// N = 4: 45 us against 66 us.
-bool wino_faster(long long N, int C, int L, int dil) {
-  if (!wino_supported(L) || dil < 1 || N < 1 || C < 1) return false;
-  const long long d = dil < L ? dil : L;
-  const bool regular = (d % 32) == 0 || (32 % d) == 0;
-  if (!regular && d < 16) return false;
-  const long long pairs = ((long long)L + 2 * d - 1) / (2 * d) * d;
-  if (5 * pairs > 3LL * L) return false;
-  const long long wgs = N * ((pairs + WPAIRS - 1) / WPAIRS) * ((C + 64 * WMB - 1) / (64 * WMB));
-  return wgs >= 256;
-}
-
-int wino_pair_tiles(int L, int dil) {
-  const long long blocks = ((long long)L + 2LL * dil - 1) / (2LL * dil);   // super-blocks
-  const long long pairs = blocks * dil;
-  return (int)((pairs + WPAIRS - 1) / WPAIRS);
-}
 
 __global__ void __launch_bounds__(NTHREADS, 2)
 conv_wino_kernel(ConvF32Args a) {

@@ -68,9 +68,12 @@ hipError_t launch_prep_wino(const float* W, int C_out, int C_in, int Cout_pad, i
                             const float* gamma, const float* beta, float eps, float* scale,
                             float* shift, hipStream_t stream);
 // conv_wino.hip: the float32 block by Winograd F(2,3) along the dilation lattice, for
-// wino_supported(L) (L_in < 2^28), taken by default when wino_faster(N, C, L, d); 32
-// output pairs per workgroup, a.n_tt = wino_pair_tiles(L, d), a.Q = Cin_pad / KC, a.dil
-// = a.pad = min(d, L)
+// wino_supported(L) (L_in < 2^28), taken by default when wino_faster(N, C, L, d) (both
+// in api.hip, with wino_pair_tiles); WINO_PAIRS output pairs and WINO_CO_TILE channels
+// per workgroup, a.n_tt = wino_pair_tiles(L, d), a.Q = Cin_pad / KC, a.dil = a.pad =
+// min(d, L)
+constexpr int WINO_PAIRS = 32;
+constexpr int WINO_CO_TILE = 256;
 bool wino_supported(int L);
 bool wino_faster(long long N, int C, int L, int dil);
 int wino_pair_tiles(int L, int dil);

@@ -151,24 +151,24 @@ def test_last_error_is_cleared_on_success():
 
 
 @pytest.mark.parametrize("N,C,L,d,method", [
-    # Winograd when 5 * pairs <= 3 * L, pairs = ceil(L / 2e) * e, e = min(d, L); e divides
-    # 32, is a multiple of 32 or is at least 16; and at least 256 workgroups
+    # Winograd when 3 * pairs <= 2 * L, pairs = ceil(L / 2e) * e, e = min(d, L), and at
+    # least 160 workgroups
     (32, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 1, dc.DCONV1D_METHOD_WINOGRAD),
     (32, 256, 4096, 8, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 2048, dc.DCONV1D_METHOD_WINOGRAD),
     (32, 256, 4096, 96, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 100, dc.DCONV1D_METHOD_WINOGRAD),
     (32, 256, 4096, 48, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 20, dc.DCONV1D_METHOD_WINOGRAD),
-    (32, 256, 4096, 3, dc.DCONV1D_METHOD_DIRECT), (32, 256, 4096, 5, dc.DCONV1D_METHOD_DIRECT),
-    (32, 256, 4096, 15, dc.DCONV1D_METHOD_DIRECT), (32, 256, 4096, 16, dc.DCONV1D_METHOD_WINOGRAD),
-    (32, 256, 4096, 1500, dc.DCONV1D_METHOD_DIRECT),   # pairs 3000: 15000 > 12288
+    (32, 256, 4096, 3, dc.DCONV1D_METHOD_WINOGRAD), (32, 256, 4096, 5, dc.DCONV1D_METHOD_WINOGRAD),
+    (32, 256, 4096, 2500, dc.DCONV1D_METHOD_WINOGRAD),  # pairs 2500: 7500 <= 8192
+    (32, 256, 4096, 1500, dc.DCONV1D_METHOD_DIRECT),    # pairs 3000: 9000 > 8192
     (32, 256, 4096, 3000, dc.DCONV1D_METHOD_DIRECT),
-    (512, 16, 7, 2, dc.DCONV1D_METHOD_WINOGRAD),       # pairs 4: 20 <= 21
-    (512, 16, 5, 2, dc.DCONV1D_METHOD_DIRECT),         # pairs 4: 20 > 15
+    (512, 16, 7, 2, dc.DCONV1D_METHOD_WINOGRAD),        # pairs 4: 12 <= 14
+    (512, 16, 5, 2, dc.DCONV1D_METHOD_DIRECT),          # pairs 4: 12 > 10
     # d >= L acts as d = L: every pair's second output lies past the end
     (512, 16, 256, 1000, dc.DCONV1D_METHOD_DIRECT), (512, 16, 1, 7, dc.DCONV1D_METHOD_DIRECT),
     (32, 256, 4096, 4096, dc.DCONV1D_METHOD_DIRECT),
-    # fewer workgroups than compute units: 64 pair tiles per sample at L = 4096, d = 128
-    (1, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT), (3, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
-    (4, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 512, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
+    # small grids: 64 pair tiles per sample at L = 4096, d = 128
+    (1, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT), (2, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
+    (3, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 512, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
     (0, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
     # lengths from 2^28 on keep the direct kernel (32-bit offsets of two rows)
     (1, 1, (1 << 28) - 1, 64, dc.DCONV1D_METHOD_WINOGRAD), (1, 1, 1 << 28, 64, dc.DCONV1D_METHOD_DIRECT),
