@@ -46,8 +46,16 @@ for _ in range(12):
 
 
 @pytest.mark.parametrize("N,C,L,d", BLOCK_SHAPES)
-@pytest.mark.parametrize("mode", ["eval", "eval_bf16", "train", "external"])
-def test_random_block(N, C, L, d, mode):
+@pytest.mark.parametrize("mode", ["eval", "eval_bf16", "train", "external", "eval_winograd",
+                                  "train_winograd", "external_winograd"])
+def test_random_block(N, C, L, d, mode, monkeypatch):
+    """The *_winograd modes run the float32 block through the Winograd kernel
+    (DCONV1D_WINOGRAD=1); these shapes are too small for the automatic choice to take it."""
+    if mode.endswith("_winograd"):
+        monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
+        mode = mode[:-len("_winograd")]
+    else:
+        monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
     seed = 90_000 + N * 1000 + C * 7 + L + d
     announce("random block", mode, (N, C, L, d), "seed", seed)
     bf16 = mode == "eval_bf16"
