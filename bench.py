@@ -107,7 +107,8 @@ def cpu_baseline(w, min_seconds: float):
 
 def _kernel_name(workload_kind, bf16, winograd=False):
     if workload_kind == "groupnorm":
-        return "conv_gn_fused_kernel<1, 4>"   # per-wave windows, 16-byte loads
+        # per-wave windows, 16-byte loads, the conv's form
+        return f"conv_gn_fused_kernel<1, 4, {'true' if winograd else 'false'}>"
     if bf16:
         return "conv_bf16_kernel<pair, 8 waves>"
     return "conv_wino_kernel (Winograd F(2,3))" if winograd else "conv_f32_kernel<128, BN, residual, float>"
@@ -121,6 +122,15 @@ def winograd_mfma_flops(N, C, L, d):
     pairs = -(-L // (2 * d)) * d
     pairs_run = -(-pairs // 32) * 32
     return 8.0 * N * (-(-C // 256) * 256) * (-(-C // 32) * 32) * pairs_run
+
+
+def groupnorm_winograd_mfma_flops(N, C_in, C_out, T_out):
+    """Multiply-add work the single-kernel Conv1d + GroupNorm path runs on the matrix cores
+    in its Winograd form: per (sample, 16 output channels), ceil(T_out / 128) waves of 64
+    output pairs, each four 16 x 16 x 4 MFMAs per pair block and K-step, four K-steps per
+    16 input channels, two flops per multiply-add."""
+    waves = -(-T_out // 128)
+    return 2.0 * N * C_out * waves * 64 * 4 * C_in
 
 
 def setup(workload, dilation, bn, dev):
@@ -197,13 +207,16 @@ def setup(workload, dilation, bn, dev):
                                     G, w["padding"], w["dilation"], out=out)
 
         flops = 2.0 * N * T_out * C_out * 3 * C_in
-        winograd, mfma_flops = False, flops
+        winograd = dc.dconv1d_groupnorm_method(N, C_in, C_out, T, G, w["padding"], w["dilation"],
+                                               x=q["x"], W=q["W"]) == dc.DCONV1D_METHOD_WINOGRAD
+        mfma_flops = groupnorm_winograd_mfma_flops(N, C_in, C_out, T_out) if winograd else flops
         # one launch (every group inside one workgroup): x once, out written once, W and
         # the affine vectors; the conv output never reaches HBM
         alg_bytes = 4.0 * (N * C_in * T + N * C_out * T_out + 3 * C_in * C_out + 2 * C_out)
         config = {"workload": wl.name, "N": N, "C_in": C_in, "C_out": C_out, "T": T,
                   "num_groups": G, "kernel_size": 3, "padding": w["padding"],
-                  "dilation": w["dilation"], "parallelism": "single GPU"}
+                  "dilation": w["dilation"], "parallelism": "single GPU",
+                  "conv_method": "winograd_f2_3" if winograd else "direct_3tap"}
     return {"step": step, "flops": flops, "mfma_flops": mfma_flops, "alg_bytes": alg_bytes,
             "config": config, "bf16": bf16, "kernel": _kernel_name(wl.kind, bf16, winograd),
             "out": out}

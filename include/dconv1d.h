@@ -246,6 +246,15 @@ int relu_dconv1d_residual_fwd_bf16(const uint16_t* xn, const float* W, const flo
  * sums and centred sums of squares to the workspace, and a second kernel merges them
  * per (sample, group) in a fixed order in double precision and normalises out in
  * place. Either way results are bitwise reproducible from run to run.
+ *
+ * On the single-kernel path, dilation 1, 2 or 4 with a per-wave input window
+ * (128 + 2*dilation + s <= 136 steps, s = (4 - padding % 4) % 4 when x is 16-byte
+ * aligned and T % 4 == 0, else 0) and W 16-byte aligned take the Winograd F(2,3) form
+ * of the conv: outputs t and t + dilation share three of their four inputs, and the
+ * pair costs four products per input channel instead of six. The environment variable
+ * DCONV1D_WINOGRAD = "0" selects the three-tap form instead (dconv1d_groupnorm_method
+ * tells which form a call takes). Both forms sum in float32 and are bitwise
+ * reproducible; their results differ in the last bits.
  */
 int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias,
                          const float* gamma, const float* beta, float eps,
@@ -287,6 +296,20 @@ int dconv1d_timer_read(double* total_ms, int64_t* launches);
 #define DCONV1D_METHOD_DIRECT 0
 #define DCONV1D_METHOD_WINOGRAD 1
 int dconv1d_block_method(int64_t N, int64_t C, int64_t L, int64_t d);
+
+/*
+ * Which form of the conv a conv1d_groupnorm_fwd call with these arguments takes:
+ * DCONV1D_METHOD_WINOGRAD or DCONV1D_METHOD_DIRECT (the three-tap kernels, on the
+ * single-kernel or the two-kernel path), by the rule given at conv1d_groupnorm_fwd, the
+ * DCONV1D_WINOGRAD override included. x and W are not dereferenced: only their alignment
+ * matters (NULL stands for buffers aligned like every device allocation). Returns
+ * DCONV1D_EINVAL for sizes conv1d_groupnorm_fwd rejects (N < 0, channels outside
+ * [1, 16384], num_groups not dividing C_out, T outside [1, 2^29), padding outside
+ * [0, 2^29), dilation < 1, T_out < 1, C*T above 2^31 - 1). Host only: no HIP call.
+ */
+int dconv1d_groupnorm_method(const float* x, const float* W, int64_t num_groups, int64_t N,
+                             int64_t C_in, int64_t C_out, int64_t T, int64_t padding,
+                             int64_t dilation);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dconv1d_timer_read.restype = ctypes.c_int
     lib.dconv1d_block_method.argtypes = [I64, I64, I64, I64]
     lib.dconv1d_block_method.restype = ctypes.c_int
+    lib.dconv1d_groupnorm_method.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [I64] * 7
+    lib.dconv1d_groupnorm_method.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -291,6 +293,20 @@ def dconv1d_block_method(N: int, C: int, L: int, d: int) -> int:
     """Which form of the conv a float32 block call of shape (N, C, L) and dilation d
     takes: DCONV1D_METHOD_WINOGRAD or DCONV1D_METHOD_DIRECT (host only, no GPU needed)."""
     code = load_library().dconv1d_block_method(int(N), int(C), int(L), int(d))
+    if code < 0:
+        _check(code)
+    return code
+
+
+def dconv1d_groupnorm_method(N: int, C_in: int, C_out: int, T: int, num_groups: int,
+                             padding: int, dilation: int, x=None, W=None) -> int:
+    """Which form of the conv conv1d_groupnorm_fwd takes for these sizes and, when given,
+    the alignment of the tensors x and W (None: aligned like every allocation):
+    DCONV1D_METHOD_WINOGRAD or DCONV1D_METHOD_DIRECT (host only, no GPU needed)."""
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    code = load_library().dconv1d_groupnorm_method(ptr(x), ptr(W), int(num_groups), int(N),
+                                                   int(C_in), int(C_out), int(T), int(padding),
+                                                   int(dilation))
     if code < 0:
         _check(code)
     return code

@@ -242,14 +242,22 @@ int wino_pair_tiles(int L, int dil) {
 
 namespace {
 
-// The float32 block's conv form: Winograd when the kernel can run the shape and is the
-// faster one. DCONV1D_WINOGRAD in the environment (read at every call) overrides that:
-// "0" the direct kernel always, "1" the Winograd kernel whenever it can run the shape
-// (e.g. to compare the two, or to test the Winograd kernel on small shapes).
-bool use_winograd(int64_t N, int C, int L, int d_eff) {
+// DCONV1D_WINOGRAD in the environment, read at every call: 0 or 1 when it is "0" or "1",
+// else -1 (unset or anything else)
+int winograd_override() {
   const char* v = std::getenv("DCONV1D_WINOGRAD");
-  if (v != nullptr && v[0] == '0' && v[1] == '\0') return false;
-  if (v != nullptr && v[0] == '1' && v[1] == '\0') return wino_supported(L);
+  if (v != nullptr && (v[0] == '0' || v[0] == '1') && v[1] == '\0') return v[0] - '0';
+  return -1;
+}
+
+// The float32 block's conv form: Winograd when the kernel can run the shape and is the
+// faster one. DCONV1D_WINOGRAD overrides that: "0" the direct kernel always, "1" the
+// Winograd kernel whenever it can run the shape (e.g. to compare the two, or to test the
+// Winograd kernel on small shapes).
+bool use_winograd(int64_t N, int C, int L, int d_eff) {
+  const int o = winograd_override();
+  if (o == 0) return false;
+  if (o == 1) return wino_supported(L);
   return wino_faster((long long)N, C, L, d_eff);
 }
 
@@ -456,6 +464,28 @@ int dconv1d_block_method(int64_t N, int64_t C, int64_t L, int64_t d) {
                                                 : DCONV1D_METHOD_DIRECT;
 }
 
+int dconv1d_groupnorm_method(const float* x, const float* W, int64_t num_groups, int64_t N,
+                             int64_t C_in, int64_t C_out, int64_t T, int64_t padding,
+                             int64_t dilation) {
+  if (N < 0 || C_in < 1 || C_in > kMaxChannels || C_out < 1 || C_out > kMaxChannels ||
+      num_groups < 1 || C_out % num_groups != 0 || T < 1 || T >= (int64_t(1) << 29) ||
+      padding < 0 || padding >= (int64_t(1) << 29) || dilation < 1)
+    return DCONV1D_EINVAL;
+  const int64_t T_out = T + 2 * padding - 2 * dilation;
+  if (T_out < 1 || C_in * T > kMaxIndex || C_out * T_out > kMaxIndex) return DCONV1D_EINVAL;
+  if (N == 0) return DCONV1D_METHOD_DIRECT;
+  // T_out >= 1 bounds dilation by T/2 + padding < 2^30
+  const int cpg = (int)(C_out / num_groups);
+  if (!gn_fused_fits(N, (int)C_in, (int)C_out, (int)T, (int)T_out, (int)padding, (int)dilation,
+                     cpg, x, W))
+    return DCONV1D_METHOD_DIRECT;
+  const int delta = gn_fused_delta((int)padding, gn_fused_vec4((int)T, x));
+  const int mg = gn_fused_groups((int)T_out, (int)dilation, delta);
+  return gn_fused_wino(mg, (int)dilation, W) && winograd_override() != 0
+             ? DCONV1D_METHOD_WINOGRAD
+             : DCONV1D_METHOD_DIRECT;
+}
+
 int prenorm_dconv1d_fwd(const float* x, const float* running_mean, const float* running_var,
                         const float* gamma, const float* beta, float eps, const float* W,
                         const float* b, float* out, int64_t N, int64_t C, int64_t L, int64_t d,
@@ -585,6 +615,8 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
     g.delta = gn_fused_delta((int)padding, g.vec4 != 0);
     g.mg = gn_fused_groups(Lo, (int)dilation, g.delta);
     g.n_cb = (int)C_out / 16;
+    // the Winograd form whenever it runs the shape, unless DCONV1D_WINOGRAD is "0"
+    g.wino = gn_fused_wino(g.mg, (int)dilation, W) && winograd_override() != 0 ? 1 : 0;
     const int slot = timer_begin(stream);
     hipError_t e = launch_conv_gn_fused(g, stream);
     timer_end(slot, stream);

@@ -32,10 +32,14 @@ struct GnFusedArgs {
   int vec4;             // 16-byte x loads, gn_fused_vec4(T, x)
   int delta;            // window start shift, gn_fused_delta(pad, vec4)
   int n_cb;             // C_out / 16
+  int wino;             // Winograd F(2,3) conv (gn_fused_wino(...)), else the three taps
 };
 int gn_fused_groups(int T_out, int dil, int delta);
 bool gn_fused_vec4(int T, const void* x);
 int gn_fused_delta(int pad, bool vec4);
+// The Winograd form runs with per-wave windows, dil 1, 2 or 4 (pairs of outputs dil apart
+// tile a wave's 128 steps) and W 16-byte aligned.
+bool gn_fused_wino(int mg, int dil, const void* W);
 bool gn_fused_fits(long long N, int C_in, int C_out, int T, int T_out, int pad, int dil, int cpg,
                    const void* x, const void* W);
 hipError_t launch_conv_gn_fused(const GnFusedArgs& a, hipStream_t stream);

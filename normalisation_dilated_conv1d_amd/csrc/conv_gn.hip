@@ -126,12 +126,14 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t rs, float* 
 }  // namespace
 
 // MG: 64-step groups of the shared staged window (the window is 64*MG steps wide), or
-// GN_PRIVATE for per-wave windows; VW: floats per lane per load (1 or 4)
-template <int MG, int VW>
+// GN_PRIVATE for per-wave windows; VW: floats per lane per load (1 or 4); WINO: the
+// Winograd form of the conv (per-wave windows only)
+template <int MG, int VW, bool WINO>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * GN_WAVES, 64 * GN_WAVES)))
 conv_gn_fused_kernel(GnFusedArgs a) {
   // MG == GN_PRIVATE: each wave stages its own window (see the file comment)
   constexpr bool PRIV = MG == GN_PRIVATE;
+  static_assert(PRIV || !WINO, "the Winograd form runs with per-wave windows");
   constexpr int RS = PRIV ? GN_PW : 64 * MG + 8;               // floats per staged row
   // private windows: a wave's area holds its 16 rows and the tail of its last load
   constexpr int WAREA = PRIV ? (GN_CI * (RS / VW) + 63) / 64 * 64 * VW : GN_CI * RS;
@@ -162,14 +164,23 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   const int tz = PRIV ? 0 : tw;               // LDS column of the wave's first output step
 
   const float* xn = a.x + (size_t)n * a.C_in * a.T;
-  // this lane's weight row: W[co0 + l16][2lq][0] (see load_w)
-  const float* __restrict__ wrow = a.W + ((size_t)(co0 + l16) * a.C_in + 2 * lq) * 3;
+  // this lane's weight row: W[co0 + l16][2lq][0], or W[co0 + l16][4lq][0] in the
+  // Winograd form (see load_w)
+  const float* __restrict__ wrow =
+      a.W + ((size_t)(co0 + l16) * a.C_in + (WINO ? 4 : 2) * lq) * 3;
 
-  f32x4 acc[GN_NB];
+  // three-tap form: block nb is output steps 16nb + l16 of the wave; Winograd form: block
+  // 4j + nb is M_j of pairs 16nb + l16
+  constexpr int NACC = WINO ? 16 : GN_NB;
+  f32x4 acc[NACC];
 #pragma unroll
-  for (int nb = 0; nb < GN_NB; ++nb)
+  for (int i = 0; i < NACC; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[nb][r] = 0.f;
+    for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+  // Winograd form: with d = dil (1, 2 or 4), wave-local pair p has first output step
+  // 2d*(p/d) + p%d and second one d later; the lane's pair 16nb + l16 starts at 32nb + tl
+  const int lgd = __builtin_ctz(a.dil);
+  const int tl = WINO ? ((l16 >> lgd) << (lgd + 1)) + (l16 & (a.dil - 1)) : 0;
 
   // Load i of a row covers window columns [64*VW*i + VW*l, +VW), input steps from
   // ws = -pad - delta on. Its byte offset, or one the range check rejects (t < 0 or past
@@ -243,9 +254,21 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   };
   const int nC = a.C_in / GN_CI;
   // A operands of chunk c: W[co0 + l16][16c + 8g + 2lq + e][k] at wrow + 48c + 24g + 3e + k,
-  // stored at index 6g + 3e + k
+  // stored at index 6g + 3e + k. Winograd form: the taps W[co0 + l16][16c + 4lq + s][k]
+  // of K-step s at index 3s + k, twelve consecutive floats (16-byte aligned: C_in is a
+  // multiple of 16 and W 16-byte aligned)
   auto load_w = [&](int c, float (&dst)[12]) {
     c = min(c, nC - 1);
+    if constexpr (WINO) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(wrow + 48 * c);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const f32x4 v = p[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * i + e] = v[e];
+      }
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const f32x2* p = reinterpret_cast<const f32x2*>(wrow + 48 * c + 24 * g);
@@ -259,10 +282,66 @@ conv_gn_fused_kernel(GnFusedArgs a) {
   };
   // B operand base of this lane: row 2lq, window column tz + l16 + delta
   const int boff = wz + 2 * lq * RS + tz + l16 + a.delta;
+  // Winograd form: row 4lq, window column tl + delta (per-wave windows: tz = 0). Kept as
+  // one integer offset from the buffer: written as a chain of pointer additions, the
+  // compiler lost track of which buffer the reads use and waited for every buffer->LDS
+  // load in flight, the next chunk's included, before each chunk.
+  const int boffw = wz + 4 * lq * RS + a.delta + tl;
   // the chunk's 96 MFMAs of this wave on buffer zb, in six steps (tap k, half g); the B
   // operands of the next step are read while the current step's MFMAs run
+  // Winograd form, the chunk's 64 MFMAs in four K-steps: step s takes input channel
+  // 16c + 4lq + s (row 4lq + s). With the lattice inputs v0..v3 = x(t - pad + m*d) of a
+  // pair (t, t + d) and its taps g:
+  //   V = (v0 - v2, v1 + v2, v2 - v1, v1 - v3),  U = (g0, (g0 + g1 + g2)/2, (g0 - g1 + g2)/2, g2),
+  //   M_j += U_j V_j;  y(t) = (M0 + M1) + M2,  y(t + d) = (M1 - M2) - M3.
+  // Input step t - pad + m*d of the wave's output step t sits at window column
+  // t + m*d + delta.
+  auto compute_w = [&](const float* zb, const float (&gv)[12]) {
+    const float* bp = zb + boffw;
+    const int d = a.dil;
+    auto read_b = [&](int st, float (&dst)[4][4]) {
+      const float* p = bp + st * RS;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[nb][m] = p[32 * nb + m * d];
+    };
+    float bx[2][4][4];
+    read_b(0, bx[0]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st + 1 < 4) read_b(st + 1, bx[(st + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const float g0 = gv[3 * st], g1 = gv[3 * st + 1], g2 = gv[3 * st + 2];
+      const float e02 = g0 + g2;
+      const float u[4] = {g0, 0.5f * (e02 + g1), 0.5f * (e02 - g1), g2};
+      // all of the step's transforms first, then its MFMAs back to back: interleaved,
+      // each MFMA waited on the VALU op that formed its operand (about 10% slower)
+      float vv[4][4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const float* v = bx[st & 1][nb];
+        vv[nb][0] = v[0] - v[2];
+        vv[nb][1] = v[1] + v[2];
+        vv[nb][2] = v[2] - v[1];
+        vv[nb][3] = v[1] - v[3];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[4 * j + nb] =
+              __builtin_amdgcn_mfma_f32_16x16x4f32(u[j], vv[nb][j], acc[4 * j + nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto compute = [&](const float* zb, const float (&wv)[12]) {
     if (!active) return;
+    if constexpr (WINO) {
+      compute_w(zb, wv);
+      return;
+    }
     const float* base = zb + boff;
     auto read_b = [&](int st, f32x2 (&dst)[GN_NB]) {
       const float* p = base + 8 * (st & 1) * RS + (st >> 1) * a.dil;
@@ -348,18 +427,33 @@ conv_gn_fused_kernel(GnFusedArgs a) {
     if (c < nC) chunk(c, zA, zB, wA, wB, xa, xb);
   }
 
-  // Epilogue. Register r of block nb holds channel co0 + 4lq + r, step tw + 16nb + l16.
+  // Epilogue. Value y[i][r] of the lane is channel co0 + 4lq + r at step tw + col[i]: in
+  // the three-tap form block i, step 16i + l16; in the Winograd form output h = i % 2 of the
+  // pair in block nb = i / 2, step 32nb + tl + h*d.
   const int cpg = a.cpg;
   const double cnt = (double)cpg * (double)a.T_out;
   float y[GN_NB][4];
+  int col[GN_NB];
   bool valid[GN_NB];
 #pragma unroll
-  for (int nb = 0; nb < GN_NB; ++nb) valid[nb] = tw + 16 * nb + l16 < a.T_out;
+  for (int i = 0; i < GN_NB; ++i) {
+    col[i] = WINO ? 32 * (i >> 1) + tl + (i & 1) * a.dil : 16 * i + l16;
+    valid[i] = tw + col[i] < a.T_out;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float bco = a.bias ? a.bias[co0 + 4 * lq + r] : 0.f;
 #pragma unroll
-    for (int nb = 0; nb < GN_NB; ++nb) y[nb][r] = acc[nb][r] + bco;
+    for (int i = 0; i < GN_NB; ++i) {
+      if constexpr (WINO) {
+        const int nb = i >> 1;
+        const float m0 = acc[nb][r], m1 = acc[4 + nb][r];
+        const float m2 = acc[8 + nb][r], m3 = acc[12 + nb][r];
+        y[i][r] = ((i & 1) ? (m1 - m2) - m3 : (m0 + m1) + m2) + bco;
+      } else {
+        y[i][r] = acc[i][r] + bco;
+      }
+    }
   }
 
   // pass 1: the group means. Every wave adds up the same partials in the same order
@@ -422,8 +516,7 @@ conv_gn_fused_kernel(GnFusedArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int nb = 0; nb < GN_NB; ++nb)
-        zA[wz + (4 * lq + r) * RS + tz + 16 * nb + l16] = y[nb][r];
+      for (int nb = 0; nb < GN_NB; ++nb) zA[wz + (4 * lq + r) * RS + tz + col[nb]] = y[nb][r];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int item = l + 64 * i;
@@ -439,7 +532,7 @@ conv_gn_fused_kernel(GnFusedArgs a) {
       float* __restrict__ orow = outn + (size_t)(co0 + 4 * lq + r) * a.T_out;
 #pragma unroll
       for (int nb = 0; nb < GN_NB; ++nb) {
-        const int t = tw + 16 * nb + l16;
+        const int t = tw + col[nb];
         if (valid[nb]) __builtin_nontemporal_store(y[nb][r], &orow[t]);
       }
     }
@@ -461,6 +554,11 @@ bool gn_fused_vec4(int T, const void* x) {
 
 int gn_fused_delta(int pad, bool vec4) { return vec4 ? (4 - pad % 4) % 4 : 0; }
 
+bool gn_fused_wino(int mg, int dil, const void* W) {
+  return mg == GN_PRIVATE && (dil == 1 || dil == 2 || dil == 4) &&
+         (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+}
+
 bool gn_fused_fits(long long N, int C_in, int C_out, int T, int T_out, int pad, int dil, int cpg,
                    const void* x, const void* W) {
   const int delta = gn_fused_delta(pad, gn_fused_vec4(T, x));
@@ -473,13 +571,28 @@ template <int VW>
 static void launch_mg(const GnFusedArgs& a, int mg, dim3 grid, dim3 block, hipStream_t stream) {
   switch (mg) {
     case GN_PRIVATE:
-      hipLaunchKernelGGL((conv_gn_fused_kernel<GN_PRIVATE, VW>), grid, block, 0, stream, a);
+      if (a.wino)
+        hipLaunchKernelGGL((conv_gn_fused_kernel<GN_PRIVATE, VW, true>), grid, block, 0, stream,
+                           a);
+      else
+        hipLaunchKernelGGL((conv_gn_fused_kernel<GN_PRIVATE, VW, false>), grid, block, 0, stream,
+                           a);
       break;
-    case 4: hipLaunchKernelGGL((conv_gn_fused_kernel<4, VW>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((conv_gn_fused_kernel<8, VW>), grid, block, 0, stream, a); break;
-    case 12: hipLaunchKernelGGL((conv_gn_fused_kernel<12, VW>), grid, block, 0, stream, a); break;
-    case 17: hipLaunchKernelGGL((conv_gn_fused_kernel<17, VW>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((conv_gn_fused_kernel<19, VW>), grid, block, 0, stream, a); break;
+    case 4:
+      hipLaunchKernelGGL((conv_gn_fused_kernel<4, VW, false>), grid, block, 0, stream, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL((conv_gn_fused_kernel<8, VW, false>), grid, block, 0, stream, a);
+      break;
+    case 12:
+      hipLaunchKernelGGL((conv_gn_fused_kernel<12, VW, false>), grid, block, 0, stream, a);
+      break;
+    case 17:
+      hipLaunchKernelGGL((conv_gn_fused_kernel<17, VW, false>), grid, block, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((conv_gn_fused_kernel<19, VW, false>), grid, block, 0, stream, a);
+      break;
   }
 }
 
@@ -491,7 +604,7 @@ hipError_t launch_conv_gn_fused(const GnFusedArgs& a, hipStream_t stream) {
   const int mg = gn_fused_groups(a.T_out, a.dil, a.delta);
   if (mg == 0 || a.mg != mg || a.vec4 != (int)v4 || a.delta != gn_fused_delta(a.pad, v4) ||
       a.T_out > 128 * GN_WAVES || a.C_in % GN_CI != 0 || a.n_cb * 16 != a.C_out || a.cpg < 1 ||
-      16 % a.cpg != 0)
+      16 % a.cpg != 0 || (a.wino && !gn_fused_wino(mg, a.dil, a.W)))
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(64 * GN_WAVES);
   if (v4)

@@ -14,7 +14,7 @@ EXPECTED = {"prenorm_dconv1d_fwd", "prenorm_dconv1d_fwd_noalloc", "prenorm_dconv
             "prenorm_dconv1d_fwd_train_bf16", "relu_dconv1d_residual_fwd",
             "relu_dconv1d_residual_fwd_bf16", "conv1d_groupnorm_fwd",
             "dconv1d_last_error", "dconv1d_release", "dconv1d_timer_enable",
-            "dconv1d_timer_read", "dconv1d_block_method"}
+            "dconv1d_timer_read", "dconv1d_block_method", "dconv1d_groupnorm_method"}
 
 FAKE_X = 0x10000000
 FAKE_OUT = 0x20000000
@@ -196,3 +196,57 @@ def test_block_method_switch_and_errors(monkeypatch):
     assert lib.dconv1d_block_method(1, 16385, 16, 1) == dc.DCONV1D_EINVAL
     assert lib.dconv1d_block_method(1, 16, 0, 1) == dc.DCONV1D_EINVAL
     assert lib.dconv1d_block_method(1, 16, 16, 0) == dc.DCONV1D_EINVAL
+
+
+class _Addr:
+    """Stands in for a tensor where only the address (its alignment) is read."""
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+GN_W, GN_D = dc.DCONV1D_METHOD_WINOGRAD, dc.DCONV1D_METHOD_DIRECT
+
+
+@pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil,x_addr,W_addr,method", [
+    # the Winograd form: single-kernel path, per-wave windows (128 + 2*dil + s <= 136,
+    # s = (4 - pad % 4) % 4 with 16-byte x loads, else 0), dil 1, 2 or 4, W 16-byte aligned
+    (16, 128, 256, 1024, 32, 1, 1, None, None, GN_W),    # the GN workload's layer
+    (2, 32, 64, 512, 8, 2, 2, None, None, GN_W),         # s = 2: 134 steps
+    (2, 16, 32, 1008, 4, 4, 4, None, None, GN_W),        # s = 0: 136 steps
+    (2, 16, 32, 1008, 4, 1, 4, None, None, GN_D),        # s = 3: 139 > 136, one shared window
+    (2, 16, 32, 1008, 4, 1, 4, 4100, None, GN_W),        # 4-byte x loads: s = 0
+    (2, 16, 32, 1004, 4, 3, 3, None, None, GN_D),        # dilation 3
+    (16, 128, 256, 1024, 32, 1, 1, None, 4104, GN_D),    # W only 8-byte aligned
+    (16, 128, 256, 1024, 32, 1, 1, None, 4100, GN_D),    # W 4-byte aligned: two kernels
+    (4, 64, 128, 2048, 16, 1, 1, None, None, GN_D),      # T_out > 1024: two kernels
+    (2, 40, 96, 333, 12, 1, 1, None, None, GN_D),        # C_in not a multiple of 16
+    (2, 128, 256, 1024, 8, 1, 1, None, None, GN_D),      # 32 channels per group
+    (0, 128, 256, 1024, 32, 1, 1, None, None, GN_D),     # nothing to compute
+])
+def test_groupnorm_method(N, C_in, C_out, T, G, pad, dil, x_addr, W_addr, method, monkeypatch):
+    monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
+    x = None if x_addr is None else _Addr(x_addr)
+    W = None if W_addr is None else _Addr(W_addr)
+    assert dc.dconv1d_groupnorm_method(N, C_in, C_out, T, G, pad, dil, x=x, W=W) == method
+
+
+def test_groupnorm_method_switch_and_errors(monkeypatch):
+    shape = (16, 128, 256, 1024, 32, 1, 1)
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "0")
+    assert dc.dconv1d_groupnorm_method(*shape) == GN_D
+    for v in ("1", "", "2"):      # "1" and anything else: the automatic choice
+        monkeypatch.setenv("DCONV1D_WINOGRAD", v)
+        assert dc.dconv1d_groupnorm_method(*shape) == GN_W
+    lib = dc.load_library()
+    ok = (32, 16, 128, 256, 1024, 1, 1)   # num_groups, N, C_in, C_out, T, padding, dilation
+    assert lib.dconv1d_groupnorm_method(None, None, *ok) == GN_W
+    for i, bad in [(1, -1), (2, 0), (2, 16385), (3, 0), (0, 0), (0, 3), (4, 0), (4, 1 << 29),
+                   (5, -1), (5, 1 << 29), (6, 0), (6, 513)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.dconv1d_groupnorm_method(None, None, *args) == dc.DCONV1D_EINVAL, (i, bad)
+    with pytest.raises(Exception):
+        dc.dconv1d_groupnorm_method(-1, 128, 256, 1024, 32, 1, 1)

@@ -57,9 +57,13 @@ def test_bf16_block_same_bits_for_both_tiles():
     assert torch.equal(full[1:2], one)
 
 
-def test_groupnorm_single_launch_same_bits_at_any_grid():
+@pytest.mark.parametrize("form", ["0", "1"])
+def test_groupnorm_single_launch_same_bits_at_any_grid(form, monkeypatch):
+    """Both conv forms of the single-launch kernel (DCONV1D_WINOGRAD=0: three taps; =1: the
+    library's choice, Winograd for this dilation-1 layer)."""
+    monkeypatch.setenv("DCONV1D_WINOGRAD", form)
     N, C_in, C_out, T, G = 40, 128, 256, 1024, 32
-    announce("grid invariance groupnorm", (N, C_in, C_out, T, G))
+    announce("grid invariance groupnorm", form, (N, C_in, C_out, T, G))
     q = to_dev(groupnorm_inputs(N, C_in, C_out, T, 90_003, with_bias=True))
 
     def gn(n0, n1):

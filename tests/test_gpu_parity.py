@@ -263,6 +263,14 @@ GN_CASES = [
 ]
 
 
+def set_form(monkeypatch, form):
+    """The conv form: the library's choice ("auto") or the three-tap kernels ("three_tap")."""
+    if form == "three_tap":
+        monkeypatch.setenv("DCONV1D_WINOGRAD", "0")
+    else:
+        monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
+
+
 def run_gn(p, G, padding, dilation):
     q = to_dev(p)
     o = dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"], G,
@@ -277,9 +285,15 @@ def oracle_gn(p, G, padding, dilation):
 
 
 @pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil,bias,affine", GN_CASES)
-def test_groupnorm_matches_oracle(N, C_in, C_out, T, G, pad, dil, bias, affine):
+@pytest.mark.parametrize("form", ["auto", "three_tap"])
+def test_groupnorm_matches_oracle(N, C_in, C_out, T, G, pad, dil, bias, affine, form,
+                                  monkeypatch):
+    """form "auto": the library's choice (the single-launch kernel takes its Winograd form
+    for dilations 1, 2 and 4 with per-wave windows); "three_tap": DCONV1D_WINOGRAD=0."""
+    set_form(monkeypatch, form)
     seed = 30_000 + N + C_in + C_out + T + G + pad + dil
-    announce("conv1d_groupnorm_fwd", (N, C_in, C_out, T, G, pad, dil, bias, affine), "seed", seed)
+    announce("conv1d_groupnorm_fwd", form, (N, C_in, C_out, T, G, pad, dil, bias, affine),
+             "seed", seed)
     p = groupnorm_inputs(N, C_in, C_out, T, seed, with_bias=bias)
     if affine is False:
         p["gamma"] = None
@@ -293,12 +307,14 @@ def test_groupnorm_matches_oracle(N, C_in, C_out, T, G, pad, dil, bias, affine):
     assert err <= TOL_F32, err
 
 
-def test_groupnorm_unaligned_x():
+@pytest.mark.parametrize("form", ["auto", "three_tap"])
+def test_groupnorm_unaligned_x(form, monkeypatch):
     """x and out only 4-byte aligned (views one float into buffers): the single-launch path
     then stages with 4-byte loads; same bar against the oracle, and the floats around out
     stay untouched."""
+    set_form(monkeypatch, form)
     N, C_in, C_out, T, G, pad, dil = 2, 32, 64, 512, 8, 1, 1
-    announce("conv1d_groupnorm_fwd unaligned x and out", (N, C_in, C_out, T, G, pad, dil))
+    announce("conv1d_groupnorm_fwd unaligned x and out", form, (N, C_in, C_out, T, G, pad, dil))
     p = groupnorm_inputs(N, C_in, C_out, T, 30_777, with_bias=True)
     q = to_dev(p)
     buf = torch.empty(N * C_in * T + 4, device="cuda")
@@ -323,12 +339,14 @@ def test_groupnorm_unaligned_x():
     (16, 128, 256, 1024, 32, 1, 1),   # the GN workload: single-launch path
     (4, 64, 128, 2048, 16, 1, 1),     # T_out > 1024: two-launch path (tile partials)
 ])
-def test_groupnorm_deterministic(shape):
+@pytest.mark.parametrize("form", ["auto", "three_tap"])
+def test_groupnorm_deterministic(shape, form, monkeypatch):
     """Bitwise-equal results over 10 calls in different launch orders: back to back, after
     another kernel, on a second stream, and after a call of another shape (which leaves
     other partials in the library's workspace on the two-launch path)."""
+    set_form(monkeypatch, form)
     N, C_in, C_out, T, G, pad, dil = shape
-    announce("conv1d_groupnorm_fwd determinism", shape)
+    announce("conv1d_groupnorm_fwd determinism", form, shape)
     q = to_dev(groupnorm_inputs(N, C_in, C_out, T, 41))
     o = to_dev(groupnorm_inputs(2, C_in, C_out, T // 2 + 3, 42))
     blk = to_dev(prenorm_inputs(2, 64, 1000, 43))
@@ -414,9 +432,11 @@ def test_workload2_dilation_sweep_full(d):
     assert err <= TOL_F32, err
 
 
-def test_workload3_groupnorm_full():
+@pytest.mark.parametrize("form", ["auto", "three_tap"])
+def test_workload3_groupnorm_full(form, monkeypatch):
+    set_form(monkeypatch, form)
     w = WORKLOADS[3].dims
-    announce("workload 3 full compare", w)
+    announce("workload 3 full compare", form, w)
     p = groupnorm_inputs(w["N"], w["C_in"], w["C_out"], w["T"], seed_for(3))
     got = run_gn(p, w["G"], w["padding"], w["dilation"]).cpu().numpy()
     err = maxrel(got, oracle_gn(p, w["G"], w["padding"], w["dilation"]))

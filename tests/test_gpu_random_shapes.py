@@ -9,7 +9,7 @@ import normalisation_dilated_conv1d_amd as dc
 import oracle
 from normalisation_dilated_conv1d_amd.inputs import groupnorm_inputs, prenorm_inputs
 
-from test_gpu_parity import TOL_BF16, TOL_F32, announce, maxrel, to_dev
+from test_gpu_parity import TOL_BF16, TOL_F32, announce, maxrel, set_form, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -99,11 +99,13 @@ def test_random_wide_bf16_block(N, C, L, d):
 
 
 @pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil,bias", GN_SHAPES + GN1_SHAPES)
-def test_random_groupnorm(N, C_in, C_out, T, G, pad, dil, bias):
+@pytest.mark.parametrize("form", ["auto", "three_tap"])
+def test_random_groupnorm(N, C_in, C_out, T, G, pad, dil, bias, form, monkeypatch):
     if T + 2 * pad - 2 * dil < 1:
         pytest.skip("empty output")
+    set_form(monkeypatch, form)
     seed = 95_000 + N + C_in + C_out + T + G
-    announce("random groupnorm", (N, C_in, C_out, T, G, pad, dil, bias), "seed", seed)
+    announce("random groupnorm", form, (N, C_in, C_out, T, G, pad, dil, bias), "seed", seed)
     p = groupnorm_inputs(N, C_in, C_out, T, seed, with_bias=bias)
     q = to_dev(p)
     out = dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"], G,

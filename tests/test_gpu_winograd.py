@@ -5,16 +5,17 @@ Shapes cover both regular pair-tile layouts (d dividing 32: 64 contiguous output
 tile; d a multiple of 32: two 32-step runs d apart), dilations with tiles that cross
 super-blocks, ragged super-blocks, L % 4 != 0 (per-element epilogue), odd chunk counts,
 two output-channel tiles, d near L, and every entry point that computes the float32
-block."""
+block. The Conv1d + GroupNorm kernel's Winograd form (dilations 1, 2 and 4 with per-wave
+windows) is checked the same way at the end."""
 import numpy as np
 import pytest
 import torch
 
 import normalisation_dilated_conv1d_amd as dc
 import oracle
-from normalisation_dilated_conv1d_amd.inputs import prenorm_inputs
+from normalisation_dilated_conv1d_amd.inputs import groupnorm_inputs, prenorm_inputs
 
-from test_gpu_parity import TOL_F32, announce, maxrel, oracle_block, run_block, to_dev
+from test_gpu_parity import TOL_F32, announce, maxrel, oracle_block, oracle_gn, run_block, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +132,63 @@ def test_automatic_choice_on_a_full_grid(monkeypatch):
         announce("prenorm_dconv1d_fwd automatic", (N, C, L, d), "method", method)
         p = prenorm_inputs(N, C, L, 67 + N)
         assert maxrel(run_block(p, d).cpu().numpy(), oracle_block(p, d)) <= TOL_F32
+
+
+GN_WINO_CASES = [
+    # (N, C_in, C_out, T, G, padding, dilation)
+    (16, 128, 256, 1024, 32, 1, 1),   # the GN workload's layer
+    (2, 32, 64, 512, 8, 2, 2),        # dilation 2, window shift 2
+    (2, 16, 32, 1008, 4, 4, 4),       # dilation 4, the widest per-wave window
+    (2, 16, 32, 1008, 4, 0, 1),       # no padding: T_out = 1006, a pair across the end
+    (1, 48, 16, 130, 16, 2, 1),       # two waves, the second with 2 steps; 16 groups
+    (3, 64, 128, 255, 8, 1, 1),       # T_out = 255: a pair whose second output is past it
+]
+
+
+@pytest.mark.parametrize("N,C_in,C_out,T,G,pad,dil", GN_WINO_CASES)
+def test_groupnorm_winograd_matches_oracle_and_three_tap(N, C_in, C_out, T, G, pad, dil,
+                                                         monkeypatch):
+    monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
+    seed = 52_000 + N * 7 + C_in + C_out * 3 + T + dil
+    announce("conv1d_groupnorm_fwd winograd", (N, C_in, C_out, T, G, pad, dil), "seed", seed)
+    p = groupnorm_inputs(N, C_in, C_out, T, seed, with_bias=True)
+    q = to_dev(p)
+    ref = oracle_gn(p, G, pad, dil)
+
+    def run():
+        o = dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"],
+                                    G, pad, dil)
+        torch.cuda.synchronize()
+        return o.cpu().numpy()
+
+    assert dc.dconv1d_groupnorm_method(N, C_in, C_out, T, G, pad, dil, x=q["x"], W=q["W"]) == \
+        dc.DCONV1D_METHOD_WINOGRAD
+    err_w = maxrel(run(), ref)
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "0")
+    assert dc.dconv1d_groupnorm_method(N, C_in, C_out, T, G, pad, dil, x=q["x"], W=q["W"]) == \
+        dc.DCONV1D_METHOD_DIRECT
+    err_d = maxrel(run(), ref)
+    announce(f"   max rel err winograd {err_w:.2e}, three-tap {err_d:.2e}")
+    assert err_w <= TOL_F32, err_w
+    assert err_d <= TOL_F32, err_d
+
+
+def test_groupnorm_w_not_16_byte_aligned_takes_three_taps(monkeypatch):
+    """The Winograd form loads a lane's twelve weights as three 16-byte loads; W only
+    8-byte aligned (a view two floats into a buffer) keeps the single-kernel path with
+    the three-tap form."""
+    monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
+    N, C_in, C_out, T, G, pad, dil = 2, 32, 64, 512, 8, 1, 1
+    announce("conv1d_groupnorm_fwd W 8-byte aligned", (N, C_in, C_out, T, G, pad, dil))
+    p = groupnorm_inputs(N, C_in, C_out, T, 52_999, with_bias=True)
+    q = to_dev(p)
+    buf = torch.empty(q["W"].numel() + 2, device="cuda")
+    W = buf[2:].view_as(q["W"])
+    W.copy_(q["W"])
+    assert W.data_ptr() % 16 == 8
+    assert dc.dconv1d_groupnorm_method(N, C_in, C_out, T, G, pad, dil, x=q["x"], W=W) == \
+        dc.DCONV1D_METHOD_DIRECT
+    out = dc.conv1d_groupnorm_fwd(q["x"], W, q["bias"], q["gamma"], q["beta"], q["eps"], G, pad,
+                                  dil)
+    torch.cuda.synchronize()
+    assert maxrel(out.cpu().numpy(), oracle_gn(p, G, pad, dil)) <= TOL_F32
