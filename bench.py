@@ -222,17 +222,25 @@ def setup(workload, dilation, bn, dev):
             "out": out}
 
 
-def timed(step, steps, warmup, dev):
+def timed(step, steps, warmup, dev, warmup_ms=0.0):
     """Mean ms per step over `steps` steps after `warmup` untimed ones (HIP events on the
     current stream), and the mean duration of the dominant kernel over another `steps`
-    steps (HIP events the library records around each launch, on its stream)."""
+    steps (HIP events the library records around each launch, on its stream). With
+    warmup_ms, more untimed steps follow the `warmup` ones until about that much GPU time
+    has passed (the GPU's clocks fall while the host prepares a workload's inputs)."""
     import torch
 
     import normalisation_dilated_conv1d_amd as dc
 
+    t0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    if warmup_ms > 0:
+        per = (time.perf_counter() - t0) * 1e3 / max(warmup, 1)
+        for _ in range(int(warmup_ms / max(per, 1e-3))):
+            step()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -282,7 +290,7 @@ def other_workloads(dev, steps, warmup):
     res = {}
     for workload, dil in ((2, 1), (2, 8), (2, 512), (2, 2048), (3, None), (4, None)):
         s = setup(workload, dil, "eval", dev)
-        ms, kms = timed(s["step"], steps, warmup, dev)
+        ms, kms = timed(s["step"], steps, warmup, dev, warmup_ms=100.0)
         rec = roofline(s["flops"], s["alg_bytes"], kms, s["bf16"], measured_traffic(workload),
                        s["mfma_flops"])
         rec["kernel"] = s["kernel"]
