@@ -111,17 +111,19 @@ def _kernel_name(workload_kind, bf16, winograd=False):
         return f"conv_gn_fused_kernel<1, 4, {'true' if winograd else 'false'}>"
     if bf16:
         return "conv_bf16_kernel<pair, 8 waves>"
-    return "conv_wino_kernel (Winograd F(2,3))" if winograd else "conv_f32_kernel<128, BN, residual, float>"
+    return ("conv_wino_kernel<4> (Winograd F(2,3), 256-channel tiles)" if winograd
+            else "conv_f32_kernel<128, 4, BN, residual, float>")
 
 
-def winograd_mfma_flops(N, C, L, d):
+def winograd_mfma_flops(N, C, L, d, co_tile=256):
     """Multiply-add work the Winograd kernel runs on the matrix cores for a float32 block:
-    four GEMMs over (output channels padded to 256) x (input channels padded to 32) x
-    (output pairs, in tiles of 32), two flops per multiply-add."""
+    four GEMMs over (output channels padded to the channel tile: 256 for the benchmark's
+    C = 256 and 512) x (input channels padded to 32) x (output pairs, in tiles of 32), two
+    flops per multiply-add."""
     d = min(d, L)
     pairs = -(-L // (2 * d)) * d
     pairs_run = -(-pairs // 32) * 32
-    return 8.0 * N * (-(-C // 256) * 256) * (-(-C // 32) * 32) * pairs_run
+    return 8.0 * N * (-(-C // co_tile) * co_tile) * (-(-C // 32) * 32) * pairs_run
 
 
 def groupnorm_winograd_mfma_flops(N, C_in, C_out, T_out):

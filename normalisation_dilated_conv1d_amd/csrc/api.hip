@@ -211,12 +211,51 @@ namespace dconv1d {
 // The kernel runs any dilation; two rows' byte offsets must fit 32 bits.
 bool wino_supported(int L) { return L >= 1 && L < (1 << 28); }
 
+// Channel tiles. Both float32 kernels take 64*mb output channels per workgroup, mb = 4, 2
+// or 1 (16-channel blocks per wave), and run their MFMAs at nearly one rate whatever the
+// tile (the smaller ones with more workgroups per CU). So the fastest tile is the one with
+// the least padded channel work, weighted by the tiles' relative rates; cost is that
+// work per unit rate (channels x 100).
+namespace {
+
+struct ChannelTile {
+  int mb;
+  long long cost;
+};
+
+ChannelTile best_channel_tile(int C, const int (&rate)[3]) {
+  static const int mbs[3] = {4, 2, 1};
+  ChannelTile best{4, -1};
+  for (int i = 0; i < 3; ++i) {
+    const long long cot = 64LL * mbs[i];
+    const long long cost = (C + cot - 1) / cot * cot * 10000 / rate[i];
+    if (best.cost < 0 || cost < best.cost) best = {mbs[i], cost};
+  }
+  return best;
+}
+
+// Relative rates of mb = 4, 2, 1. Direct kernel, measured on C = 256 and 512 (N = 32,
+// L = 4096, d = 128): 1 : 0.98 : 0.95. On that shape with C = 64 the direct kernel took
+// 38 us with mb = 1 against 119 us with mb = 4, C = 192 249 against 311 us, C = 320 661
+// against 992 us (mb = 2: 764 us), while C = 256 stays at mb = 4 (407 against 430 us).
+constexpr int kRateDirect[3] = {100, 98, 95};
+// Winograd kernel, measured the same way (C = 256: 297, 309, 320 us; C = 512 at N = 16:
+// 576, 602, 622 us): 1 : 0.96 : 0.93. With C = 64 it took 33 us with mb = 1 against 90 us
+// with mb = 4, C = 128 88 us with mb = 2 (mb = 1: 90, mb = 4: 157), C = 192 187 us with
+// mb = 1 against 229 us, C = 320 492 us with mb = 1 against 716 us.
+constexpr int kRateWino[3] = {100, 96, 93};
+
+}  // namespace
+
+int wino_channel_blocks(int C) { return best_channel_tile(C, kRateWino).mb; }
+
 // Whether the Winograd form is the faster one. It computes 4 products per output pair
 // and input channel, over every pair of the super-blocks that cover [0, L); the direct
-// form 3 per output step, and it runs its MFMAs at a higher rate (about 0.81 of the peak
-// against 0.74). So the Winograd form needs at most 2L/3 pairs (every dilation up to L/2
-// that tiles L into whole super-blocks gives L/2; dilations close to L or above it give
-// more, as most pairs' second output then lies past the end), and a grid of at least 160
+// form 3 per output step, and at equal channel tiles it runs its MFMAs at a higher rate
+// (about 0.81 of the peak against 0.74). So the Winograd form needs at most 2L/3 pairs
+// (every dilation up to L/2 that tiles L into whole super-blocks gives L/2; dilations
+// close to L or above it give more, as most pairs' second output then lies past the
+// end), scaled by the two forms' channel-tile costs, and a grid of at least 160
 // workgroups (5/8 of the CUs), below which the direct kernel's smaller tiles fill the
 // chip better. Measured on C=256 L=4096 against the direct kernel's 404 us at N=32:
 // d = 3 to 300 348-373 us, d = 2500 (P = 0.61 L) 382 us, d = 1500 (P = 0.73 L) 453 us;
@@ -226,10 +265,26 @@ bool wino_faster(long long N, int C, int L, int dil) {
   if (!wino_supported(L) || dil < 1 || N < 1 || C < 1) return false;
   const long long d = dil < L ? dil : L;
   const long long pairs = ((long long)L + 2 * d - 1) / (2 * d) * d;
-  if (3 * pairs > 2LL * L) return false;
-  const long long wgs =
-      N * ((pairs + WINO_PAIRS - 1) / WINO_PAIRS) * ((C + WINO_CO_TILE - 1) / WINO_CO_TILE);
+  const ChannelTile w = best_channel_tile(C, kRateWino);
+  const ChannelTile f = best_channel_tile(C, kRateDirect);
+  if (3 * pairs * w.cost > 2LL * L * f.cost) return false;
+  const long long cot = 64LL * w.mb;
+  const long long wgs = N * ((pairs + WINO_PAIRS - 1) / WINO_PAIRS) * ((C + cot - 1) / cot);
   return wgs >= 160;
+}
+
+// Tile shape of the direct float32 kernel: the channel tile above with 128 time steps when
+// that gives at least two workgroups per CU (512), else with 64; when even that leaves
+// one wave per SIMD, half the channel tile (more, smaller workgroups, each x tile read
+// once more), down to 64 channels.
+ConvTile conv_f32_tile(int L_out, int N, int C_out) {
+  auto wgs = [&](int tt, int cot) {
+    return (long long)N * ((L_out + tt - 1) / tt) * ((C_out + cot - 1) / cot);
+  };
+  for (int mb = best_channel_tile(C_out, kRateDirect).mb;; mb /= 2) {
+    if (wgs(128, 64 * mb) >= 512) return {128, mb};
+    if (wgs(64, 64 * mb) >= 512 || mb == 1) return {64, mb};
+  }
 }
 
 int wino_pair_tiles(int L, int dil) {
@@ -360,15 +415,16 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   // keeps every tap offset inside int range.
   const int d_eff = (int)std::min<int64_t>(d, L);
   // float32 storage takes the Winograd kernel when use_winograd says so (32 output pairs
-  // and 256 channels per tile), else the direct kernel with the tile conv_f32_tile picks; bf16 storage runs the bf16-MFMA kernel: 64-channel
-  // K-chunks, 128-step time tiles (a 256- or 512-channel tile). The repacked weights are
-  // padded to whole channel tiles.
+  // and the channel tile wino_channel_blocks picks), else the direct kernel with the tile
+  // conv_f32_tile picks; bf16 storage runs the bf16-MFMA kernel: 64-channel K-chunks,
+  // 128-step time tiles (a 256- or 512-channel tile). The repacked weights are padded to
+  // whole 256-channel tiles (every smaller tile divides 256).
   const bool wino = !bf16 && use_winograd(N, Ci, Li, d_eff);
   const int Cin_pad = round_up(Ci, bf16 ? CIN_PAD_BF16 : KC);
   const int co_tile_bf16 = bf16 ? conv_bf16_co_tile(N, Li, Ci) : 0;
   const int Cout_pad = round_up(Ci, bf16 ? co_tile_bf16 : CO_TILE_F32);
   const ConvTile tile = bf16 ? ConvTile{TILE_T_BF16, co_tile_bf16 / 64}
-                        : wino ? ConvTile{0, CO_TILE_F32 / 64}
+                        : wino ? ConvTile{0, wino_channel_blocks(Ci)}
                                : conv_f32_tile(Li, (int)std::min<int64_t>(N, kMaxIndex), Ci);
   const int n_ct = (Ci + tile.co_tile() - 1) / tile.co_tile();
   const int n_tt = wino ? wino_pair_tiles(Li, d_eff) : (Li + tile.tt - 1) / tile.tt;
@@ -445,7 +501,7 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
   e = bf16 ? launch_conv_bf16(a, tile.co_tile(), stream)
-      : wino ? launch_conv_wino(a, stream)
+      : wino ? launch_conv_wino(a, tile.mb, stream)
              : launch_conv_f32(a, tile, EPI_RESIDUAL, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");

@@ -13,8 +13,8 @@
 // W[co][ci][k] * z[ci][t - pad + k*dil], i.e. M = C_out, N = time, K = 3*C_in.
 //
 // Work split
-//   workgroup  = one sample n, 64*MB output channels (co tile: 256 or 128), TT time steps
-//                (t tile: 128 or 64); 4 waves, wave w owns output channels
+//   workgroup  = one sample n, 64*MB output channels (co tile: 256, 128 or 64), TT time
+//                steps (t tile: 128 or 64); 4 waves, wave w owns output channels
 //                [16*MB*w, 16*MB*(w+1)) of the co tile and all TT time steps: MB x (TT/16)
 //                MFMA 16x16 accumulator blocks.
 //   K loop     = chunks of 32 input channels of one tap, ordered (ci-block, tap) so
@@ -375,19 +375,6 @@ conv_f32_kernel(ConvF32Args a) {
   }
 }
 
-// Tile shape. Largest first: 128 time steps x 256 channels (4 accumulator blocks of 16
-// channels per wave) when that gives at least two workgroups per CU (512); otherwise 64
-// time steps; and when even that leaves one wave per SIMD, 64 x 128 channels (2 blocks
-// per wave), which doubles the waves at the cost of reading each x tile twice.
-ConvTile conv_f32_tile(int L_out, int N, int C_out) {
-  auto wgs = [&](int tt, int cot) {
-    return (long long)N * ((L_out + tt - 1) / tt) * ((C_out + cot - 1) / cot);
-  };
-  if (wgs(128, 256) >= 512) return {128, 4};
-  if (wgs(64, 256) >= 512) return {64, 4};
-  return {64, 2};
-}
-
 template <int TT, int MB, bool BN, int EPI, typename XT>
 static hipError_t launch_one(const ConvF32Args& a, int nwg, hipStream_t stream) {
   hipLaunchKernelGGL((conv_f32_kernel<TT, MB, BN, EPI, XT>), dim3(nwg), dim3(NTHREADS), 0, stream,
@@ -400,6 +387,9 @@ static hipError_t launch_shape(const ConvF32Args& a, ConvTile tile, int nwg, hip
   if (tile.tt == 128 && tile.mb == 4) return launch_one<128, 4, BN, EPI, float>(a, nwg, stream);
   if (tile.tt == 64 && tile.mb == 4) return launch_one<64, 4, BN, EPI, float>(a, nwg, stream);
   if (tile.tt == 64 && tile.mb == 2) return launch_one<64, 2, BN, EPI, float>(a, nwg, stream);
+  if (tile.tt == 128 && tile.mb == 2) return launch_one<128, 2, BN, EPI, float>(a, nwg, stream);
+  if (tile.tt == 128 && tile.mb == 1) return launch_one<128, 1, BN, EPI, float>(a, nwg, stream);
+  if (tile.tt == 64 && tile.mb == 1) return launch_one<64, 1, BN, EPI, float>(a, nwg, stream);
   return hipErrorInvalidValue;
 }
 

@@ -22,9 +22,10 @@
 // and the epilogue goes through LDS. Any other dilation takes the per-element epilogue.
 //
 // Work split
-//   workgroup  = one sample n, 256 output channels, 32 pairs (64 output steps); 4 waves,
-//                wave w owns output channels [64w, 64w + 64): for each of the four
-//                transforms j, 4 x 2 MFMA 16x16 accumulator blocks (128 registers).
+//   workgroup  = one sample n, 64*WMB output channels (WMB = 4, 2 or 1: 256, 128 or 64),
+//                32 pairs (64 output steps); 4 waves, wave w owns output channels
+//                [16*WMB*w, 16*WMB*(w + 1)): for each of the four transforms j, WMB x 2
+//                MFMA 16x16 accumulator blocks (128 registers at WMB = 4).
 //   K loop     = chunks of 32 input channels (no taps: they are inside the transform),
 //                8 MFMA steps of K = 4 each, 32 MFMAs per step.
 //   B operand  = V_j[32 rows][32 pairs] staged through LDS per chunk by all 256 threads:
@@ -60,7 +61,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int WPAIRS = WINO_PAIRS;        // output pairs per workgroup
 constexpr int WPITCH = 4 * WPAIRS + 4;    // floats per staged row (four V_j per pair)
 constexpr int WEP = 2 * WPAIRS + 4;       // floats per epilogue row (64 output steps)
-constexpr int WMB = WINO_CO_TILE / 64;    // 16-channel blocks per wave
 constexpr int WNB = WPAIRS / 16;          // 16-pair blocks per wave
 constexpr int WRPL = KC * WPAIRS / NTHREADS;   // staged (row, pair) items per thread (4)
 
@@ -81,6 +81,8 @@ __device__ __forceinline__ int wino_tile_start(int pt, int d) {
 
 }  // namespace
 
+// WMB: 16-channel blocks per wave (the workgroup's channel tile is 64*WMB: 256, 128 or 64)
+template <int WMB>
 __global__ void __launch_bounds__(NTHREADS, 2)
 conv_wino_kernel(ConvF32Args a) {
   constexpr int CO_TILE = 64 * WMB;
@@ -351,16 +353,23 @@ conv_wino_kernel(ConvF32Args a) {
   }
 }
 
-hipError_t launch_conv_wino(const ConvF32Args& a, hipStream_t stream) {
+hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, hipStream_t stream) {
   const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.scale == nullptr || a.C_in != a.C_out || a.L_in != a.L_out || a.pad != a.dil ||
       !wino_supported(a.L_in) || a.dil < 1 || a.dil > a.L_in ||
       a.n_tt != wino_pair_tiles(a.L_in, a.dil) ||
-      a.NCB * 16 < a.n_ct * 64 * WMB || a.Q * KC < a.C_in)
+      (wmb != 1 && wmb != 2 && wmb != 4) || a.n_ct != (a.C_out + 64 * wmb - 1) / (64 * wmb) ||
+      a.NCB * 16 < a.n_ct * 64 * wmb || a.Q * KC < a.C_in)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(conv_wino_kernel, dim3((unsigned)nwg), dim3(NTHREADS), 0, stream, a);
+  const dim3 grid((unsigned)nwg), block(NTHREADS);
+  if (wmb == 4)
+    hipLaunchKernelGGL(conv_wino_kernel<4>, grid, block, 0, stream, a);
+  else if (wmb == 2)
+    hipLaunchKernelGGL(conv_wino_kernel<2>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(conv_wino_kernel<1>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -69,15 +69,15 @@ hipError_t launch_prep_wino(const float* W, int C_out, int C_in, int Cout_pad, i
                             float* shift, hipStream_t stream);
 // conv_wino.hip: the float32 block by Winograd F(2,3) along the dilation lattice, for
 // wino_supported(L) (L_in < 2^28), taken by default when wino_faster(N, C, L, d) (both
-// in api.hip, with wino_pair_tiles); WINO_PAIRS output pairs and WINO_CO_TILE channels
-// per workgroup, a.n_tt = wino_pair_tiles(L, d), a.Q = Cin_pad / KC, a.dil = a.pad =
-// min(d, L)
+// in api.hip, with wino_pair_tiles and wino_channel_blocks); WINO_PAIRS output pairs and
+// 64*wmb channels (wmb = 4, 2 or 1) per workgroup, a.n_tt = wino_pair_tiles(L, d),
+// a.n_ct = ceil(C / (64*wmb)), a.Q = Cin_pad / KC, a.dil = a.pad = min(d, L)
 constexpr int WINO_PAIRS = 32;
-constexpr int WINO_CO_TILE = 256;
 bool wino_supported(int L);
 bool wino_faster(long long N, int C, int L, int dil);
 int wino_pair_tiles(int L, int dil);
-hipError_t launch_conv_wino(const ConvF32Args& a, hipStream_t stream);
+int wino_channel_blocks(int C);
+hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, hipStream_t stream);
 
 // conv_bf16.hip: 64-channel K-chunks, input channels padded to a multiple of 128 (an
 // even chunk count), 128 time steps per tile

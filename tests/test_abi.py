@@ -170,6 +170,11 @@ def test_last_error_is_cleared_on_success():
     (1, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT), (2, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
     (3, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 512, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
     (0, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
+    # channel counts off multiples of 256: both kernels take 64- or 128-channel tiles, so
+    # the grid condition counts those; the costs keep the Winograd form
+    (32, 64, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (32, 320, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
+    (3, 64, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 64, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
+    (2, 320, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),    # five 64-channel tiles: 640 workgroups
     # lengths from 2^28 on keep the direct kernel (32-bit offsets of two rows)
     (1, 1, (1 << 28) - 1, 64, dc.DCONV1D_METHOD_WINOGRAD), (1, 1, 1 << 28, 64, dc.DCONV1D_METHOD_DIRECT),
     (1, 1, (1 << 30) - 1, 64, dc.DCONV1D_METHOD_DIRECT),

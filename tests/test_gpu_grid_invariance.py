@@ -1,9 +1,9 @@
 """Results must not depend on how many workgroups a launch has: the same samples computed
 alone and inside larger batches give bitwise-equal outputs. The batch sizes are chosen so
 that the library picks a different tile (and so a different grid and workgroup shape) for
-each: for the float32 block's direct kernel at C=256, L=4096 the 64x128 tile below N=8, the
-64x256 tile for 8 <= N < 16 and the 128x256 tile from N=16 (and the Winograd kernel's grid
-at each N); for the bf16 block at C=512, L=16384 the
+each: for the float32 block's direct kernel at C=256, L=4096 the 64x64 tile below N=4, the
+64x128 tile for 4 <= N < 8, the 64x256 tile for 8 <= N < 16 and the 128x256 tile from
+N=16 (and the Winograd kernel's grid at each N); for the bf16 block at C=512, L=16384 the
 256-channel tile at N=1 and the 512-channel tile from N=2; and for Conv1d+GroupNorm the
 single-launch kernel at 16 and at 640 workgroups. Every output is a fixed sequence of MFMA
 steps over the same K order whatever the tile, so equal bits are the bar. A missing
@@ -39,10 +39,12 @@ def test_f32_block_same_bits_for_every_tile(form, monkeypatch):
     q = to_dev(prenorm_inputs(N, C, L, 90_001))
     full = _block(q, 0, N, d)                 # 128 x 256 tiles, 640 workgroups
     mid = _block(q, 2, 12, d)                 # N = 10: 64 x 256 tiles
-    small = _block(q, 3, 6, d)                # N = 3: 64 x 128 tiles
+    five = _block(q, 7, 12, d)                # N = 5: 64 x 128 tiles
+    small = _block(q, 3, 6, d)                # N = 3: 64 x 64 tiles
     one = _block(q, 19, 20, d)                # N = 1
     torch.cuda.synchronize()
     assert torch.equal(full[2:12], mid)
+    assert torch.equal(full[7:12], five)
     assert torch.equal(full[3:6], small)
     assert torch.equal(full[19:20], one)
 

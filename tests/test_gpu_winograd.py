@@ -192,3 +192,25 @@ def test_groupnorm_w_not_16_byte_aligned_takes_three_taps(monkeypatch):
                                   dil)
     torch.cuda.synchronize()
     assert maxrel(out.cpu().numpy(), oracle_gn(p, G, pad, dil)) <= TOL_F32
+
+
+SMALL_C_CASES = [
+    # (N, C, L, d): channel counts below 256 and between multiples of it take 64- and
+    # 128-channel tiles in both kernels (a workgroup per CU or more)
+    (32, 64, 4096, 128),      # direct 128-step x 64-channel tiles; Winograd 64-channel tiles
+    (16, 128, 4096, 128),     # direct 128 x 128; Winograd 128-channel tiles
+    (8, 192, 4096, 8),        # three 64-channel tiles
+    (4, 320, 2048, 100),      # five 64-channel tiles; per-element Winograd epilogue
+]
+
+
+@pytest.mark.parametrize("N,C,L,d", SMALL_C_CASES)
+@pytest.mark.parametrize("form", ["0", "1"])
+def test_small_channel_tiles_match_oracle(N, C, L, d, form, monkeypatch):
+    monkeypatch.setenv("DCONV1D_WINOGRAD", form)
+    seed = 54_000 + N + C + L + d
+    announce("prenorm_dconv1d_fwd channel tiles", form, (N, C, L, d), "seed", seed)
+    p = prenorm_inputs(N, C, L, seed)
+    err = maxrel(run_block(p, d).cpu().numpy(), oracle_block(p, d))
+    announce(f"   max rel err {err:.2e}")
+    assert err <= TOL_F32, err
