@@ -289,8 +289,9 @@ int dconv1d_timer_read(double* total_ms, int64_t* launches);
  * costs (each kernel takes 64*mb channels per workgroup, mb = 4, 2 or 1, whichever
  * minimises the padded channels divided by the tile's relative rate: 1, 0.96, 0.93 for
  * the Winograd kernel, 1, 0.98, 0.95 for the direct one; c_w = c_d when C is a multiple
- * of 256); and N * ceil(P / 32) * ceil(C / (64*mb)) >= 160 (workgroups for 5/8 of the
- * compute units); else DCONV1D_METHOD_DIRECT. The environment variable DCONV1D_WINOGRAD, read at every call,
+ * of 256); else DCONV1D_METHOD_DIRECT. On grids of fewer than two workgroups per compute
+ * unit both kernels halve their channel tile (down to 64), which keeps the Winograd form
+ * the faster one there too. The environment variable DCONV1D_WINOGRAD, read at every call,
  * overrides this: "0" selects the direct form always, "1" the Winograd form for every
  * L < 2^28. Returns DCONV1D_EINVAL for N < 0, C outside [1, 16384], L < 1 or d < 1.
  * Host only: no HIP call. Each form gives a sample the same bits at any N; as the

@@ -247,7 +247,25 @@ constexpr int kRateWino[3] = {100, 96, 93};
 
 }  // namespace
 
-int wino_channel_blocks(int C) { return best_channel_tile(C, kRateWino).mb; }
+namespace {
+
+long long wino_pairs(int L, int dil) {
+  const long long d = dil < L ? dil : L;
+  return ((long long)L + 2 * d - 1) / (2 * d) * d;
+}
+
+}  // namespace
+
+// Channel tile of the Winograd kernel: the cheapest one by the cost above, halved while
+// the grid has fewer than two workgroups per CU (512), as the direct kernel does: at
+// N = 1 and 2 (C = 256, L = 4096, d = 128) 64-channel tiles took 21 and 28 us against 44
+// and 44 us with 256-channel tiles (the direct kernel's best: 25 and 37 us).
+int wino_channel_blocks(long long N, int C, int L, int dil) {
+  const long long pair_tiles = (wino_pairs(L, dil) + WINO_PAIRS - 1) / WINO_PAIRS;
+  int mb = best_channel_tile(C, kRateWino).mb;
+  while (mb > 1 && N * pair_tiles * ((C + 64LL * mb - 1) / (64LL * mb)) < 512) mb /= 2;
+  return mb;
+}
 
 // Whether the Winograd form is the faster one. It computes 4 products per output pair
 // and input channel, over every pair of the super-blocks that cover [0, L); the direct
@@ -255,22 +273,18 @@ int wino_channel_blocks(int C) { return best_channel_tile(C, kRateWino).mb; }
 // (about 0.81 of the peak against 0.74). So the Winograd form needs at most 2L/3 pairs
 // (every dilation up to L/2 that tiles L into whole super-blocks gives L/2; dilations
 // close to L or above it give more, as most pairs' second output then lies past the
-// end), scaled by the two forms' channel-tile costs, and a grid of at least 160
-// workgroups (5/8 of the CUs), below which the direct kernel's smaller tiles fill the
-// chip better. Measured on C=256 L=4096 against the direct kernel's 404 us at N=32:
-// d = 3 to 300 348-373 us, d = 2500 (P = 0.61 L) 382 us, d = 1500 (P = 0.73 L) 453 us;
-// at d = 128: N = 1 and 2 (64 and 128 workgroups) 44 us against 38-39 us, N = 3 (192)
-// 45 us against 65 us.
+// end), scaled by the two forms' channel-tile costs. Measured on C=256 L=4096 against the
+// direct kernel's 404 us at N=32: d = 3 to 300 348-373 us, d = 2500 (P = 0.61 L) 382 us,
+// d = 1500 (P = 0.73 L) 453 us. Small grids take smaller channel tiles in both kernels
+// (wino_channel_blocks, conv_f32_tile), and the Winograd form stays ahead there too:
+// N = 1, 2 at d = 128 above; N = 1, C = 512, L = 4096, d = 8: 48 against 67 us; N = 4,
+// C = 128, L = 1024, d = 16: 13 against 15 us; N = 2, C = 64, L = 2048, d = 4: 9.3
+// against 10.1 us.
 bool wino_faster(long long N, int C, int L, int dil) {
   if (!wino_supported(L) || dil < 1 || N < 1 || C < 1) return false;
-  const long long d = dil < L ? dil : L;
-  const long long pairs = ((long long)L + 2 * d - 1) / (2 * d) * d;
   const ChannelTile w = best_channel_tile(C, kRateWino);
   const ChannelTile f = best_channel_tile(C, kRateDirect);
-  if (3 * pairs * w.cost > 2LL * L * f.cost) return false;
-  const long long cot = 64LL * w.mb;
-  const long long wgs = N * ((pairs + WINO_PAIRS - 1) / WINO_PAIRS) * ((C + cot - 1) / cot);
-  return wgs >= 160;
+  return 3 * wino_pairs(L, dil) * w.cost <= 2LL * L * f.cost;
 }
 
 // Tile shape of the direct float32 kernel: the channel tile above with 128 time steps when
@@ -424,7 +438,7 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   const int co_tile_bf16 = bf16 ? conv_bf16_co_tile(N, Li, Ci) : 0;
   const int Cout_pad = round_up(Ci, bf16 ? co_tile_bf16 : CO_TILE_F32);
   const ConvTile tile = bf16 ? ConvTile{TILE_T_BF16, co_tile_bf16 / 64}
-                        : wino ? ConvTile{0, wino_channel_blocks(Ci)}
+                        : wino ? ConvTile{0, wino_channel_blocks(N, Ci, Li, d_eff)}
                                : conv_f32_tile(Li, (int)std::min<int64_t>(N, kMaxIndex), Ci);
   const int n_ct = (Ci + tile.co_tile() - 1) / tile.co_tile();
   const int n_tt = wino ? wino_pair_tiles(Li, d_eff) : (Li + tile.tt - 1) / tile.tt;

@@ -59,7 +59,6 @@ struct ConvTile {
   int tt, mb;
   int co_tile() const { return 64 * mb; }
 };
-ConvTile conv_f32_tile(int L_out, int N, int C_out);
 hipError_t launch_conv_f32(const ConvF32Args& a, ConvTile tile, int epilogue, hipStream_t stream);
 
 // prep.hip: BN fold + the Winograd weight transform, [Cin_pad/4 steps][Cout_pad/16][64] x 4
@@ -68,15 +67,13 @@ hipError_t launch_prep_wino(const float* W, int C_out, int C_in, int Cout_pad, i
                             const float* gamma, const float* beta, float eps, float* scale,
                             float* shift, hipStream_t stream);
 // conv_wino.hip: the float32 block by Winograd F(2,3) along the dilation lattice, for
-// wino_supported(L) (L_in < 2^28), taken by default when wino_faster(N, C, L, d) (both
-// in api.hip, with wino_pair_tiles and wino_channel_blocks); WINO_PAIRS output pairs and
-// 64*wmb channels (wmb = 4, 2 or 1) per workgroup, a.n_tt = wino_pair_tiles(L, d),
-// a.n_ct = ceil(C / (64*wmb)), a.Q = Cin_pad / KC, a.dil = a.pad = min(d, L)
+// wino_supported(L) (L_in < 2^28; defined in api.hip with wino_pair_tiles and the choice
+// of form and tiles); WINO_PAIRS output pairs and 64*wmb channels (wmb = 4, 2 or 1) per
+// workgroup, a.n_tt = wino_pair_tiles(L, d), a.n_ct = ceil(C / (64*wmb)),
+// a.Q = Cin_pad / KC, a.dil = a.pad = min(d, L)
 constexpr int WINO_PAIRS = 32;
 bool wino_supported(int L);
-bool wino_faster(long long N, int C, int L, int dil);
 int wino_pair_tiles(int L, int dil);
-int wino_channel_blocks(int C);
 hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, hipStream_t stream);
 
 // conv_bf16.hip: 64-channel K-chunks, input channels padded to a multiple of 128 (an

@@ -166,14 +166,17 @@ def test_last_error_is_cleared_on_success():
     # d >= L acts as d = L: every pair's second output lies past the end
     (512, 16, 256, 1000, dc.DCONV1D_METHOD_DIRECT), (512, 16, 1, 7, dc.DCONV1D_METHOD_DIRECT),
     (32, 256, 4096, 4096, dc.DCONV1D_METHOD_DIRECT),
-    # small grids: 64 pair tiles per sample at L = 4096, d = 128
-    (1, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT), (2, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
+    # small grids: both kernels halve their channel tiles, and the rule does not count
+    # workgroups
+    (1, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
     (3, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 512, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
+    (1, 16, 62, 40, dc.DCONV1D_METHOD_WINOGRAD),        # pairs 40: 3 * 40 * 6881 <= 2 * 62 * 6736
+    (1, 16, 62, 50, dc.DCONV1D_METHOD_DIRECT),          # pairs 50: over it
     (0, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
     # channel counts off multiples of 256: both kernels take 64- or 128-channel tiles, so
     # the grid condition counts those; the costs keep the Winograd form
     (32, 64, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (32, 320, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
-    (3, 64, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 64, 4096, 128, dc.DCONV1D_METHOD_DIRECT),
+    (3, 64, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD), (2, 64, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
     (2, 320, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),    # five 64-channel tiles: 640 workgroups
     # lengths from 2^28 on keep the direct kernel (32-bit offsets of two rows)
     (1, 1, (1 << 28) - 1, 64, dc.DCONV1D_METHOD_WINOGRAD), (1, 1, 1 << 28, 64, dc.DCONV1D_METHOD_DIRECT),
@@ -193,7 +196,7 @@ def test_block_method_switch_and_errors(monkeypatch):
     assert dc.dconv1d_block_method(1, 16, 1 << 28, 1) == dc.DCONV1D_METHOD_DIRECT
     for v in ("", "2", "yes"):    # anything else: the automatic choice
         monkeypatch.setenv("DCONV1D_WINOGRAD", v)
-        assert dc.dconv1d_block_method(1, 16, 62, 1) == dc.DCONV1D_METHOD_DIRECT
+        assert dc.dconv1d_block_method(1, 16, 62, 50) == dc.DCONV1D_METHOD_DIRECT
         assert dc.dconv1d_block_method(32, 256, 4096, 128) == dc.DCONV1D_METHOD_WINOGRAD
     lib = dc.load_library()
     assert lib.dconv1d_block_method(-1, 16, 16, 1) == dc.DCONV1D_EINVAL

@@ -3,7 +3,7 @@ alone and inside larger batches give bitwise-equal outputs. The batch sizes are 
 that the library picks a different tile (and so a different grid and workgroup shape) for
 each: for the float32 block's direct kernel at C=256, L=4096 the 64x64 tile below N=4, the
 64x128 tile for 4 <= N < 8, the 64x256 tile for 8 <= N < 16 and the 128x256 tile from
-N=16 (and the Winograd kernel's grid at each N); for the bf16 block at C=512, L=16384 the
+N=16 (and the Winograd kernel's grid and channel tile at each N); for the bf16 block at C=512, L=16384 the
 256-channel tile at N=1 and the 512-channel tile from N=2; and for Conv1d+GroupNorm the
 single-launch kernel at 16 and at 640 workgroups. Every output is a fixed sequence of MFMA
 steps over the same K order whatever the tile, so equal bits are the bar. A missing

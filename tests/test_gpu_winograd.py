@@ -122,12 +122,14 @@ def test_winograd_training_mode_and_caller_normalised(monkeypatch):
     assert maxrel(got.cpu().numpy(), ref) <= TOL_F32
 
 
-def test_automatic_choice_on_a_full_grid(monkeypatch):
-    """Without the override, a shape with a workgroup per compute unit takes the Winograd
-    form and one with fewer the direct form; both against the oracle."""
+def test_automatic_choice(monkeypatch):
+    """Without the override, a regular dilation takes the Winograd form on a full grid and
+    on a one-sample grid (64-channel tiles), a dilation near L the direct form; all against
+    the oracle."""
     monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
     for N, C, L, d, method in ((4, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
-                               (1, 256, 4096, 128, dc.DCONV1D_METHOD_DIRECT)):
+                               (1, 256, 4096, 128, dc.DCONV1D_METHOD_WINOGRAD),
+                               (1, 256, 4096, 1500, dc.DCONV1D_METHOD_DIRECT)):
         assert dc.dconv1d_block_method(N, C, L, d) == method
         announce("prenorm_dconv1d_fwd automatic", (N, C, L, d), "method", method)
         p = prenorm_inputs(N, C, L, 67 + N)
