@@ -373,14 +373,19 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # per-step durations (median), warm and with the MALL flushed: before each cold step a
-    # 512 MiB scratch buffer is overwritten, so x (134 MB for the default workload) does
-    # not stay resident in the 256 MB last-level cache between steps
+    # 512 MiB scratch buffer is overwritten ("write"), so x (134 MB for the default
+    # workload) does not stay resident in the 256 MB last-level cache between steps, and
+    # the caches hold the scratch's dirty lines, written back while the step runs; or it
+    # is read ("read": summed), which also evicts x but leaves nothing to write back
     def per_step_ms(flush):
-        scratch = torch.empty(512 * (1 << 20) // 4, device=dev) if flush else None
+        scratch = torch.ones(512 * (1 << 20) // 4, device=dev) if flush else None
+        sink = torch.empty((), device=dev)
         times = []
         for i in range(args.steps):
-            if flush:
+            if flush == "write":
                 scratch.fill_(float(i))
+            elif flush == "read":
+                torch.sum(scratch, dim=0, out=sink)
             a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a_ev.record(stream)
             step()
@@ -391,8 +396,9 @@ def main():
         del scratch
         return ms[len(ms) // 2]
 
-    warm_median = per_step_ms(False)
-    cold_median = per_step_ms(True)
+    warm_median = per_step_ms(None)
+    cold_median = per_step_ms("write")
+    cold_read_median = per_step_ms("read")
 
     # dominant kernel alone: HIP events recorded by the library around each launch of
     # the fused conv kernel, on the stream it is launched on
@@ -441,6 +447,7 @@ def main():
         "hbm_gbps_algorithmic": round(gbps, 2),
         "ms_per_step_median": round(warm_median, 5),
         "ms_per_step_median_cold_mall": round(cold_median, 5),
+        "ms_per_step_median_cold_mall_read": round(cold_read_median, 5),
         "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": rl,
     }
