@@ -377,28 +377,35 @@ def main():
     # workload) does not stay resident in the 256 MB last-level cache between steps, and
     # the caches hold the scratch's dirty lines, written back while the step runs; or it
     # is read ("read": summed), which also evicts x but leaves nothing to write back
+    # Each also returns the conv kernel's mean duration over those steps (the library's
+    # event pair around each launch).
     def per_step_ms(flush):
+        import normalisation_dilated_conv1d_amd as dc
+
         scratch = torch.ones(512 * (1 << 20) // 4, device=dev) if flush else None
         sink = torch.empty((), device=dev)
         times = []
-        for i in range(args.steps):
-            if flush == "write":
-                scratch.fill_(float(i))
-            elif flush == "read":
-                torch.sum(scratch, dim=0, out=sink)
-            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_ev.record(stream)
-            step()
-            b_ev.record(stream)
-            times.append((a_ev, b_ev))
-        torch.cuda.synchronize()
+        with dc.KernelTimer() as kt:
+            for i in range(args.steps):
+                if flush == "write":
+                    scratch.fill_(float(i))
+                elif flush == "read":
+                    torch.sum(scratch, dim=0, out=sink)
+                a_ev = torch.cuda.Event(enable_timing=True)
+                b_ev = torch.cuda.Event(enable_timing=True)
+                a_ev.record(stream)
+                step()
+                b_ev.record(stream)
+                times.append((a_ev, b_ev))
+            torch.cuda.synchronize()
+            k_ms, k_n = kt.read()
         ms = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in times)
         del scratch
-        return ms[len(ms) // 2]
+        return ms[len(ms) // 2], k_ms / max(k_n, 1)
 
-    warm_median = per_step_ms(None)
-    cold_median = per_step_ms("write")
-    cold_read_median = per_step_ms("read")
+    warm_median, _ = per_step_ms(None)
+    cold_median, cold_kern = per_step_ms("write")
+    cold_read_median, cold_read_kern = per_step_ms("read")
 
     # dominant kernel alone: HIP events recorded by the library around each launch of
     # the fused conv kernel, on the stream it is launched on
@@ -448,6 +455,8 @@ def main():
         "ms_per_step_median": round(warm_median, 5),
         "ms_per_step_median_cold_mall": round(cold_median, 5),
         "ms_per_step_median_cold_mall_read": round(cold_read_median, 5),
+        "kernel_ms_cold_mall": round(cold_kern, 5),
+        "kernel_ms_cold_mall_read": round(cold_read_kern, 5),
         "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": rl,
     }
