@@ -214,8 +214,8 @@ bool wino_supported(int L) { return L >= 1 && L < (1 << 28); }
 // Channel tiles. Both float32 kernels take 64*mb output channels per workgroup, mb = 4, 2
 // or 1 (16-channel blocks per wave), and run their MFMAs at nearly one rate whatever the
 // tile (the smaller ones with more workgroups per CU). So the fastest tile is the one with
-// the least padded channel work, weighted by the tiles' relative rates; cost is that
-// work per unit rate (channels x 100).
+// the least padded channel work, weighted by the tiles' relative rates; a tile's cost is
+// its padded channel count divided by its rate (times 100).
 namespace {
 
 struct ChannelTile {
@@ -245,10 +245,7 @@ constexpr int kRateDirect[3] = {100, 98, 95};
 // mb = 1 against 229 us, C = 320 492 us with mb = 1 against 716 us.
 constexpr int kRateWino[3] = {100, 96, 93};
 
-}  // namespace
-
-namespace {
-
+// output pairs of the Winograd form: every pair of the super-blocks that cover [0, L)
 long long wino_pairs(int L, int dil) {
   const long long d = dil < L ? dil : L;
   return ((long long)L + 2 * d - 1) / (2 * d) * d;
