@@ -247,6 +247,10 @@ int relu_dconv1d_residual_fwd_bf16(const uint16_t* xn, const float* W, const flo
  * per (sample, group) in a fixed order in double precision and normalises out in
  * place. Either way results are bitwise reproducible from run to run.
  *
+ * The conv of the two-kernel path is Winograd F(2,3) too (see below) when padding equals
+ * dilation and the rule of dconv1d_block_method, applied to (N, C_out, T, dilation),
+ * picks that form.
+ *
  * On the single-kernel path, dilation 1, 2 or 4 with a per-wave input window
  * (128 + 2*dilation + s <= 136 steps, s = (4 - padding % 4) % 4 when x is 16-byte
  * aligned and T % 4 == 0, else 0) and W 16-byte aligned take the Winograd F(2,3) form
@@ -304,8 +308,8 @@ int dconv1d_block_method(int64_t N, int64_t C, int64_t L, int64_t d);
 
 /*
  * Which form of the conv a conv1d_groupnorm_fwd call with these arguments takes:
- * DCONV1D_METHOD_WINOGRAD or DCONV1D_METHOD_DIRECT (the three-tap kernels, on the
- * single-kernel or the two-kernel path), by the rule given at conv1d_groupnorm_fwd, the
+ * DCONV1D_METHOD_WINOGRAD or DCONV1D_METHOD_DIRECT (the three-tap kernels), on the
+ * single-kernel or the two-kernel path, by the rules given at conv1d_groupnorm_fwd, the
  * DCONV1D_WINOGRAD override included. x and W are not dereferenced: only their alignment
  * matters (NULL stands for buffers aligned like every device allocation). Returns
  * DCONV1D_EINVAL for sizes conv1d_groupnorm_fwd rejects (N < 0, channels outside

@@ -327,6 +327,16 @@ bool use_winograd(int64_t N, int C, int L, int d_eff) {
   return wino_faster((long long)N, C, L, d_eff);
 }
 
+// The conv form of the two-kernel Conv1d + GroupNorm path: the Winograd kernel needs the
+// block's lattice, padding = dilation (so T_out = T), and is taken as for the block (the
+// channel tiles follow C_out); DCONV1D_WINOGRAD overrides the same way. Sizes as
+// validated by conv1d_groupnorm_fwd (T < 2^29).
+bool gn_two_kernel_winograd(int64_t N, int64_t C_out, int64_t T, int64_t padding,
+                            int64_t dilation) {
+  if (padding != dilation) return false;
+  return use_winograd(N, (int)C_out, (int)T, (int)std::min<int64_t>(dilation, T));
+}
+
 // ---------------------------------------------------------------- shared checks
 constexpr int64_t kMaxChannels = 16384;
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
@@ -512,7 +522,7 @@ int prenorm_common(const XT* x, const XT* residual, const float* running_mean,
   a.n_ct = n_ct;
   const int slot = timer_begin(stream);
   e = bf16 ? launch_conv_bf16(a, tile.co_tile(), stream)
-      : wino ? launch_conv_wino(a, tile.mb, stream)
+      : wino ? launch_conv_wino(a, tile.mb, EPI_RESIDUAL, stream)
              : launch_conv_f32(a, tile, EPI_RESIDUAL, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
@@ -545,7 +555,8 @@ int dconv1d_groupnorm_method(const float* x, const float* W, int64_t num_groups,
   const int cpg = (int)(C_out / num_groups);
   if (!gn_fused_fits(N, (int)C_in, (int)C_out, (int)T, (int)T_out, (int)padding, (int)dilation,
                      cpg, x, W))
-    return DCONV1D_METHOD_DIRECT;
+    return gn_two_kernel_winograd(N, C_out, T, padding, dilation) ? DCONV1D_METHOD_WINOGRAD
+                                                                   : DCONV1D_METHOD_DIRECT;
   const int delta = gn_fused_delta((int)padding, gn_fused_vec4((int)T, x));
   const int mg = gn_fused_groups((int)T_out, (int)dilation, delta);
   return gn_fused_wino(mg, (int)dilation, W) && winograd_override() != 0
@@ -691,9 +702,19 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
     return DCONV1D_OK;
   }
 
+  // Two kernels: the conv (Winograd when gn_two_kernel_winograd says so, else the direct
+  // kernel with the tile above) writes y into out and per-(channel, tile) statistics into
+  // the workspace, then gn_normalize_kernel merges them per group and normalises out.
+  const bool wino = gn_two_kernel_winograd(N, C_out, T, padding, dilation);
+  const int d_w = (int)std::min<int64_t>(dilation, T);
+  const int wmb = wino ? wino_channel_blocks(N, (int)C_out, (int)T, d_w) : 0;
+  const int n_tt_c = wino ? wino_pair_tiles((int)T, d_w) : n_tt;
+  const int n_ct_c = wino ? ((int)C_out + 64 * wmb - 1) / (64 * wmb) : n_ct;
+  if (N * n_tt_c * n_ct_c > kMaxIndex) return fail(DCONV1D_EINVAL, "grid too large");
   const size_t off_wp = 0;
-  const size_t off_part = align256(off_wp + sizeof(float) * 3 * (size_t)Cin_pad * Cout_pad);
-  const size_t total = align256(off_part + sizeof(float) * 2 * (size_t)N * C_out * n_tt);
+  const size_t off_part =
+      align256(off_wp + sizeof(float) * (wino ? 4 : 3) * (size_t)Cin_pad * Cout_pad);
+  const size_t total = align256(off_part + sizeof(float) * 3 * (size_t)N * C_out * n_tt_c);
   char* ws = nullptr;
   WorkspaceUse use;
   int st = use.acquire(total, stream, &ws);
@@ -701,8 +722,11 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
   float* Wp = reinterpret_cast<float*>(ws + off_wp);
   float* part = reinterpret_cast<float*>(ws + off_part);
 
-  hipError_t e = launch_prep_f32(W, (int)C_out, (int)C_in, Cout_pad, Cin_pad, Wp, nullptr,
-                                 nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream);
+  hipError_t e =
+      wino ? launch_prep_wino(W, (int)C_out, (int)C_in, Cout_pad, Cin_pad, Wp, nullptr, nullptr,
+                              nullptr, nullptr, 0.f, nullptr, nullptr, stream)
+           : launch_prep_f32(W, (int)C_out, (int)C_in, Cout_pad, Cin_pad, Wp, nullptr, nullptr,
+                             nullptr, nullptr, 0.f, nullptr, nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "prep kernel launch");
 
   // dilation > T + 2*padding would already make T_out < 1, so taps fit in int
@@ -719,18 +743,21 @@ int conv1d_groupnorm_fwd(const float* x, const float* W, const float* bias, cons
   a.C_out = (int)C_out;
   a.L_in = (int)T;
   a.L_out = Lo;
-  a.pad = (int)padding;
-  a.dil = (int)dilation;
+  // the Winograd form: padding = dilation, both taken as min(dilation, T) (dilations from
+  // T on leave only the centre tap either way)
+  a.pad = wino ? d_w : (int)padding;
+  a.dil = wino ? d_w : (int)dilation;
   a.NCB = Cout_pad / 16;
-  a.Q = 3 * Cin_pad / KC;
-  a.n_tt = n_tt;
-  a.n_ct = n_ct;
+  a.Q = (wino ? 1 : 3) * Cin_pad / KC;
+  a.n_tt = n_tt_c;
+  a.n_ct = n_ct_c;
   const int slot = timer_begin(stream);
-  e = launch_conv_f32(a, tile, EPI_GN_STATS, stream);
+  e = wino ? launch_conv_wino(a, wmb, EPI_GN_STATS, stream)
+           : launch_conv_f32(a, tile, EPI_GN_STATS, stream);
   timer_end(slot, stream);
   if (e != hipSuccess) return hip_fail(e, "conv kernel launch");
   e = launch_gn_normalize(out, part, gamma, beta, eps, (int)N, (int)C_out, Lo, (int)num_groups,
-                          n_tt, tile.tt, stream);
+                          n_tt_c, stream);
   if (e != hipSuccess) return hip_fail(e, "groupnorm kernel launch");
   return DCONV1D_OK;
 }

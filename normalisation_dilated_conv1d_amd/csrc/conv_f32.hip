@@ -361,9 +361,10 @@ conv_f32_kernel(ConvF32Args a) {
         m2 = quarterwave_sum(m2);
         if (cok) {
           if (l16 == 0) {
-            float* p = a.partials + (((size_t)n * a.C_out + co) * a.n_tt + tt) * 2;
+            float* p = a.partials + (((size_t)n * a.C_out + co) * a.n_tt + tt) * 3;
             p[0] = s;
             p[1] = m2;
+            p[2] = (float)cnt;
           }
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {

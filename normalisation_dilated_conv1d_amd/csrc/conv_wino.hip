@@ -64,6 +64,23 @@ constexpr int WEP = 2 * WPAIRS + 4;       // floats per epilogue row (64 output 
 constexpr int WNB = WPAIRS / 16;          // 16-pair blocks per wave
 constexpr int WRPL = KC * WPAIRS / NTHREADS;   // staged (row, pair) items per thread (4)
 
+// v of the lane K places further along its DPP row of 16 lanes (row_ror:K)
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 | K, 0xF, 0xF, false));
+}
+
+// sum over the 16 lanes of each quarter-wave (a DPP row); lanes associate the terms
+// differently, so where the bits matter one lane's value is used
+__device__ __forceinline__ float quarterwave_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return v;
+}
+
 // first output step of pair p
 __device__ __forceinline__ int wino_pair_step(int p, int d) {
   const int b = p / d;
@@ -81,8 +98,12 @@ __device__ __forceinline__ int wino_tile_start(int pt, int d) {
 
 }  // namespace
 
-// WMB: 16-channel blocks per wave (the workgroup's channel tile is 64*WMB: 256, 128 or 64)
-template <int WMB>
+// WMB: 16-channel blocks per wave (the workgroup's channel tile is 64*WMB: 256, 128 or 64).
+// BN: the staged value is ReLU(BN(x)) (the block) or x itself (the conv of Conv1d +
+// GroupNorm). EPI: EPI_RESIDUAL (the block: + bias + residual) or EPI_GN_STATS (y = conv
+// + bias into out, and per (channel, pair tile) the sum, the tile-centred sum of squares
+// and the count of y for the GroupNorm pass).
+template <int WMB, bool BN, int EPI>
 __global__ void __launch_bounds__(NTHREADS, 2)
 conv_wino_kernel(ConvF32Args a) {
   constexpr int CO_TILE = 64 * WMB;
@@ -135,7 +156,8 @@ conv_wino_kernel(ConvF32Args a) {
   const int t0c = regular ? T0 + ((c >> lgD) << (lgD + 1)) + (c & (D - 1))
                           : wino_pair_step(WPAIRS * pt + c, d);
   uint32_t toff[4];                         // byte offsets inside a row
-  float cap[4];
+  float cap[4];                             // BN: +inf inside the input, 0 on padding
+  uint32_t keep[4];                         // no BN: all ones inside the input, 0 on padding
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int t = t0c + (m - 1) * d;      // |t| < 2^30: L, d < 2^28
@@ -143,7 +165,11 @@ conv_wino_kernel(ConvF32Args a) {
     // an outside step loads any in-range step: its cap makes it zero
     toff[m] = 4u * (uint32_t)(in ? t : 0);
     cap[m] = in ? __builtin_huge_valf() : 0.f;
-    asm volatile("" : "+v"(cap[m]));
+    keep[m] = in ? 0xffffffffu : 0u;
+    if (BN)
+      asm volatile("" : "+v"(cap[m]));
+    else
+      asm volatile("" : "+v"(keep[m]));
   }
   const int zpos = 64 * (c >> 4) + 4 * (c & 15);   // LDS position of the pair in a row
 
@@ -162,17 +188,24 @@ conv_wino_kernel(ConvF32Args a) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         xr[i][m] = *reinterpret_cast<const float*>(rowp + (ro + toff[m]));
-      sc[i] = a.scale[KC * q + 8 * w + 2 * i + hrow];
-      sh[i] = a.shift[KC * q + 8 * w + 2 * i + hrow];
+      if (BN) {
+        sc[i] = a.scale[KC * q + 8 * w + 2 * i + hrow];
+        sh[i] = a.shift[KC * q + 8 * w + 2 * i + hrow];
+      }
     }
   };
-  auto store_z = [&](float* dst) {
+  // chunk q's staged values: with BN, med3(fma(x, scale, shift), 0, cap) (a padded input
+  // channel has scale = shift = 0); without, x AND a mask that is zero on a padded tap
+  // or a padded input channel
+  auto store_z = [&](int q, float* dst) {
 #pragma unroll
     for (int i = 0; i < WRPL; ++i) {
       float z[4];
+      const uint32_t rkeep = KC * q + 8 * w + 2 * i + hrow < a.C_in ? 0xffffffffu : 0u;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        z[m] = __builtin_amdgcn_fmed3f(fmaf(xr[i][m], sc[i], sh[i]), 0.f, cap[m]);
+        z[m] = BN ? __builtin_amdgcn_fmed3f(fmaf(xr[i][m], sc[i], sh[i]), 0.f, cap[m])
+                  : __uint_as_float(__float_as_uint(xr[i][m]) & keep[m] & rkeep);
       f32x4 v;
       v[0] = z[0] - z[2];
       v[1] = z[1] + z[2];
@@ -233,18 +266,18 @@ conv_wino_kernel(ConvF32Args a) {
   load_a(0, 0, au[0]);
   load_a(0, 1, au[1]);
   load_x(0);
-  store_z(zs0);
+  store_z(0, zs0);
   __syncthreads();
   int q = 0;
   for (; q + 1 < Q; q += 2) {
     load_x(q + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(zs0, q, [&] { store_z(zs1); });
+    compute(zs0, q, [&] { store_z(q + 1, zs1); });
     __syncthreads();
     const int qn = min(q + 2, Q - 1);
     load_x(qn);
     __builtin_amdgcn_sched_barrier(0);
-    compute(zs1, q + 1, [&] { store_z(zs0); });
+    compute(zs1, q + 1, [&] { store_z(qn, zs0); });
     __syncthreads();
   }
   if (q < Q) compute(zs0, q, [] {});
@@ -255,8 +288,70 @@ conv_wino_kernel(ConvF32Args a) {
   // pair c: o0 = 2D*(c / D) + c % D and o0 + D; its step is T0 + o, or T0 + d + (o - 32)
   // for o >= 32 when d > 32.
   float* outn = reinterpret_cast<float*>(a.out) + (size_t)n * a.C_out * L;
-  const float* resn = reinterpret_cast<const float*>(a.residual) + (size_t)n * a.C_out * L;
   const int co_w = ct * CO_TILE + 16 * WMB * w;
+  if (EPI == EPI_GN_STATS) {
+    // y = conv + bias into out, and per output channel the tile's sum S of y, the sum of
+    // squares about the tile mean and the count, at partials[((n*C_out + co)*n_tt + pt)*3].
+    // Registers (j, mb, nb, r) of the 16 lanes of quarter-wave lq hold channel
+    // 16mb + 4lq + r at all 32 pairs of the tile, so each sum runs over those 16 lanes
+    // (DPP row rotations), and lane 0 of the row gives S to the row before the second
+    // pass.
+    int ta[WNB];
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) {
+      const int cc = 16 * nb + l16;
+      ta[nb] = regular ? T0 + ((cc >> lgD) << (lgD + 1)) + (cc & (D - 1))
+                       : wino_pair_step(WPAIRS * pt + cc, d);
+    }
+    float cnt = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) cnt += (ta[nb] < L ? 1.f : 0.f) + (ta[nb] + d < L ? 1.f : 0.f);
+    // whole numbers up to 64, exact in every lane; 0 for a tile whose pairs all lie past
+    // the end (the last tile of a dilation that does not divide its super-blocks evenly)
+    cnt = quarterwave_sum(cnt);
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int co = co_w + 16 * mb + 4 * lq + r;
+        const float bco = (co < a.C_out && a.bias) ? a.bias[co] : 0.f;
+        float y[WNB][2];
+        float sum = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) {
+          const float m0 = acc[0][mb][nb][r], m1 = acc[1][mb][nb][r];
+          const float m2 = acc[2][mb][nb][r], m3 = acc[3][mb][nb][r];
+          y[nb][0] = ((m0 + m1) + m2) + bco;
+          y[nb][1] = ((m1 - m2) - m3) + bco;
+          sum += (ta[nb] < L ? y[nb][0] : 0.f) + (ta[nb] + d < L ? y[nb][1] : 0.f);
+        }
+        sum = __shfl(quarterwave_sum(sum), 16 * lq);
+        const float mean = cnt > 0.f ? sum / cnt : 0.f;
+        float m2s = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) {
+          const float d0 = y[nb][0] - mean, d1 = y[nb][1] - mean;
+          m2s += (ta[nb] < L ? d0 * d0 : 0.f) + (ta[nb] + d < L ? d1 * d1 : 0.f);
+        }
+        m2s = quarterwave_sum(m2s);
+        if (co < a.C_out) {
+#pragma unroll
+          for (int nb = 0; nb < WNB; ++nb) {
+            if (ta[nb] < L) outn[(size_t)co * L + ta[nb]] = y[nb][0];
+            if (ta[nb] + d < L) outn[(size_t)co * L + ta[nb] + d] = y[nb][1];
+          }
+          if (l16 == 0) {
+            float* pp = a.partials + (((size_t)n * a.C_out + co) * a.n_tt + pt) * 3;
+            pp[0] = sum;
+            pp[1] = m2s;
+            pp[2] = cnt;
+          }
+        }
+      }
+    }
+    return;
+  }
+  const float* resn = reinterpret_cast<const float*>(a.residual) + (size_t)n * a.C_out * L;
   const int skip = d > 32 ? d - 32 : 0;
   const bool vec_epi = regular && ((L & 3) == 0) &&
                        (((reinterpret_cast<uintptr_t>(a.out) |
@@ -353,23 +448,36 @@ conv_wino_kernel(ConvF32Args a) {
   }
 }
 
-hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, hipStream_t stream) {
+template <bool BN, int EPI>
+static void launch_wmb(const ConvF32Args& a, int wmb, dim3 grid, dim3 block,
+                       hipStream_t stream) {
+  if (wmb == 4)
+    hipLaunchKernelGGL((conv_wino_kernel<4, BN, EPI>), grid, block, 0, stream, a);
+  else if (wmb == 2)
+    hipLaunchKernelGGL((conv_wino_kernel<2, BN, EPI>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((conv_wino_kernel<1, BN, EPI>), grid, block, 0, stream, a);
+}
+
+hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, int epilogue, hipStream_t stream) {
   const long long nwg = (long long)a.N * a.n_tt * a.n_ct;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.scale == nullptr || a.C_in != a.C_out || a.L_in != a.L_out || a.pad != a.dil ||
+  // the block: BN folded into scale/shift, a residual of the output's shape; Conv1d +
+  // GroupNorm: no BN, the partials array
+  const bool block_ok = epilogue == EPI_RESIDUAL && a.scale != nullptr && a.C_in == a.C_out;
+  const bool gn_ok = epilogue == EPI_GN_STATS && a.scale == nullptr && a.partials != nullptr;
+  if (!(block_ok || gn_ok) || a.L_in != a.L_out || a.pad != a.dil ||
       !wino_supported(a.L_in) || a.dil < 1 || a.dil > a.L_in ||
       a.n_tt != wino_pair_tiles(a.L_in, a.dil) ||
       (wmb != 1 && wmb != 2 && wmb != 4) || a.n_ct != (a.C_out + 64 * wmb - 1) / (64 * wmb) ||
       a.NCB * 16 < a.n_ct * 64 * wmb || a.Q * KC < a.C_in)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(NTHREADS);
-  if (wmb == 4)
-    hipLaunchKernelGGL(conv_wino_kernel<4>, grid, block, 0, stream, a);
-  else if (wmb == 2)
-    hipLaunchKernelGGL(conv_wino_kernel<2>, grid, block, 0, stream, a);
+  if (block_ok)
+    launch_wmb<true, EPI_RESIDUAL>(a, wmb, grid, block, stream);
   else
-    hipLaunchKernelGGL(conv_wino_kernel<1>, grid, block, 0, stream, a);
+    launch_wmb<false, EPI_GN_STATS>(a, wmb, grid, block, stream);
   return hipGetLastError();
 }
 

@@ -3,8 +3,9 @@
 // normalises the conv output in place and applies gamma/beta when present).
 //
 // Here the conv kernel has already written, per (sample n, channel co, time tile),
-// the tile sum S and the tile-centred sum of squares M2 (two-pass inside the tile, in
-// registers). Each workgroup of this kernel first merges the partials of its (n, group)
+// the tile sum S, the tile-centred sum of squares M2 (two-pass inside the tile, in
+// registers) and the tile's count of outputs (direct kernel: a run of time steps;
+// Winograd kernel: the in-range outputs of its 32 output pairs). Each workgroup of this kernel first merges the partials of its (n, group)
 // in a fixed order, in double precision:
 //     mean = sum S / count
 //     M2   = sum over tiles of [ M2_tile + cnt_tile * (S_tile/cnt_tile - mean)^2 ]
@@ -50,7 +51,7 @@ constexpr int GN_MAX_ROWS = 256;
 __global__ void __launch_bounds__(256)
 gn_normalize_kernel(float* __restrict__ out, const float* __restrict__ partials,
                     const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
-                    int C_out, int L_out, int G, int n_tt, int tile_t, int rows_per_wg,
+                    int C_out, int L_out, int G, int n_tt, int rows_per_wg,
                     int chunks, int vec4) {
   const int ng = blockIdx.x / chunks;
   const int chunk = blockIdx.x - ng * chunks;
@@ -64,17 +65,18 @@ gn_normalize_kernel(float* __restrict__ out, const float* __restrict__ partials,
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int P = cpg * n_tt;  // partial entries of this group, e = c_local*n_tt + tt
-    const float* pp = partials + ((size_t)n * C_out + (size_t)g * cpg) * n_tt * 2;
+    const float* pp = partials + ((size_t)n * C_out + (size_t)g * cpg) * n_tt * 3;
     const double count = (double)cpg * (double)L_out;
     double s = 0.0;
-    for (int e = lane; e < P; e += 64) s += (double)pp[2 * e];
+    for (int e = lane; e < P; e += 64) s += (double)pp[3 * e];
     const double mean = wave_sum_d(s) / count;
     double m2 = 0.0;
     for (int e = lane; e < P; e += 64) {
-      const int tt = e % n_tt;
-      const double cnt = (double)min(tile_t, L_out - tt * tile_t);
-      const double dm = (double)pp[2 * e] / cnt - mean;
-      m2 += (double)pp[2 * e + 1] + cnt * dm * dm;
+      const double cnt = (double)pp[3 * e + 2];   // 0 for a tile with no output in range
+      if (cnt > 0.0) {
+        const double dm = (double)pp[3 * e] / cnt - mean;
+        m2 += (double)pp[3 * e + 1] + cnt * dm * dm;
+      }
     }
     const double var = wave_sum_d(m2) / count;
     const double rstd = 1.0 / sqrt(var + (double)eps);
@@ -116,7 +118,7 @@ gn_normalize_kernel(float* __restrict__ out, const float* __restrict__ partials,
 
 hipError_t launch_gn_normalize(float* out, const float* partials, const float* gamma,
                                const float* beta, float eps, int N, int C_out, int L_out,
-                               int num_groups, int n_tt, int tile_t, hipStream_t stream) {
+                               int num_groups, int n_tt, hipStream_t stream) {
   const int cpg = C_out / num_groups;
   int rows = 8192 / L_out;
   if (rows < 1) rows = 1;
@@ -127,7 +129,7 @@ hipError_t launch_gn_normalize(float* out, const float* partials, const float* g
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(gn_normalize_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, out,
-                     partials, gamma, beta, eps, C_out, L_out, num_groups, n_tt, tile_t, rows,
+                     partials, gamma, beta, eps, C_out, L_out, num_groups, n_tt, rows,
                      chunks, (int)(((L_out & 3) == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0)));
   return hipGetLastError();
 }

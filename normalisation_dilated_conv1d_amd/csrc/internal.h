@@ -25,7 +25,8 @@ struct ConvF32Args {
   const void* residual;  // [N][C_out][L_out], same storage type as out; added by the
                          // residual epilogue (x for the block). May equal out exactly:
                          // each element is read by the thread that then writes it.
-  float* partials;       // GroupNorm: [N][C_out][n_tt][2] (tile sum, centred sum of squares)
+  float* partials;       // GroupNorm: [N][C_out][n_tt][3] (tile sum, centred sum of
+                         // squares, count)
   int N, C_in, C_out, L_in, L_out;
   int pad, dil;          // tap k reads input t - pad + k*dil
   int NCB;               // 16-channel output blocks in the repacked weights (Cout_pad/16)
@@ -74,7 +75,9 @@ hipError_t launch_prep_wino(const float* W, int C_out, int C_in, int Cout_pad, i
 constexpr int WINO_PAIRS = 32;
 bool wino_supported(int L);
 int wino_pair_tiles(int L, int dil);
-hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, hipStream_t stream);
+// epilogue EPI_RESIDUAL (the block: BN in a.scale/a.shift, C_in == C_out) or EPI_GN_STATS
+// (the conv of Conv1d + GroupNorm: a.scale null, partials [N][C_out][n_tt][3])
+hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, int epilogue, hipStream_t stream);
 
 // conv_bf16.hip: 64-channel K-chunks, input channels padded to a multiple of 128 (an
 // even chunk count), 128 time steps per tile
@@ -104,9 +107,9 @@ hipError_t launch_bn_train(const void* x, bool bf16, int N, int C, int L, int Ci
                            float* save_mean, float* save_invstd, float* scale, float* shift,
                            hipStream_t stream);
 
-// gn.hip
+// gn.hip: partials [N][C_out][n_tt][3] (tile sum, centred sum of squares, count)
 hipError_t launch_gn_normalize(float* out, const float* partials, const float* gamma,
                                const float* beta, float eps, int N, int C_out, int L_out,
-                               int num_groups, int n_tt, int tile_t, hipStream_t stream);
+                               int num_groups, int n_tt, hipStream_t stream);
 
 }  // namespace dconv1d

@@ -228,10 +228,15 @@ GN_W, GN_D = dc.DCONV1D_METHOD_WINOGRAD, dc.DCONV1D_METHOD_DIRECT
     (2, 16, 32, 1008, 4, 1, 4, 4100, None, GN_W),        # 4-byte x loads: s = 0
     (2, 16, 32, 1004, 4, 3, 3, None, None, GN_D),        # dilation 3
     (16, 128, 256, 1024, 32, 1, 1, None, 4104, GN_D),    # W only 8-byte aligned
-    (16, 128, 256, 1024, 32, 1, 1, None, 4100, GN_D),    # W 4-byte aligned: two kernels
-    (4, 64, 128, 2048, 16, 1, 1, None, None, GN_D),      # T_out > 1024: two kernels
-    (2, 40, 96, 333, 12, 1, 1, None, None, GN_D),        # C_in not a multiple of 16
-    (2, 128, 256, 1024, 8, 1, 1, None, None, GN_D),      # 32 channels per group
+    # the two-kernel path: the Winograd conv when padding = dilation, else three taps
+    (16, 128, 256, 1024, 32, 1, 1, None, 4100, GN_W),    # W 4-byte aligned: two kernels
+    (4, 64, 128, 2048, 16, 1, 1, None, None, GN_W),      # T_out > 1024
+    (2, 40, 96, 333, 12, 1, 1, None, None, GN_W),        # C_in not a multiple of 16
+    (2, 128, 256, 1024, 8, 1, 1, None, None, GN_W),      # 32 channels per group
+    (4, 32, 256, 2050, 16, 0, 1, None, None, GN_D),      # padding 0, dilation 1
+    (2, 16, 48, 400, 4, 100, 100, None, None, GN_W),     # 12 channels per group
+    (2, 16, 48, 300, 4, 400, 400, None, None, GN_D),     # dilation past T: pairs = T
+    (2, 16, 48, 3000, 4, 3, 2, None, None, GN_D),        # padding != dilation
     (0, 128, 256, 1024, 32, 1, 1, None, None, GN_D),     # nothing to compute
 ])
 def test_groupnorm_method(N, C_in, C_out, T, G, pad, dil, x_addr, W_addr, method, monkeypatch):

@@ -216,3 +216,42 @@ def test_small_channel_tiles_match_oracle(N, C, L, d, form, monkeypatch):
     err = maxrel(run_block(p, d).cpu().numpy(), oracle_block(p, d))
     announce(f"   max rel err {err:.2e}")
     assert err <= TOL_F32, err
+
+
+GN_TWO_KERNEL_CASES = [
+    # (N, C_in, C_out, T, G, padding = dilation): shapes the single kernel does not take
+    (4, 64, 128, 2048, 16, 1),        # T_out > 1024
+    (2, 40, 96, 333, 12, 1),          # C_in not a multiple of 16, ragged pair tile
+    (2, 128, 256, 1024, 8, 1),        # 32 channels per group
+    (2, 16, 48, 400, 4, 100),         # 12 channels per group, pairs 100 apart
+    (1, 48, 300, 3001, 3, 5),         # C_out 300 (64-channel tiles), irregular dilation
+    (2, 32, 64, 2500, 4, 64),         # regular dilation, two 32-step runs per tile
+]
+
+
+@pytest.mark.parametrize("N,C_in,C_out,T,G,d", GN_TWO_KERNEL_CASES)
+def test_groupnorm_two_kernel_winograd(N, C_in, C_out, T, G, d, monkeypatch):
+    """The two-kernel path's Winograd conv (GroupNorm statistics per pair tile) against
+    the oracle and against its three-tap conv."""
+    monkeypatch.delenv("DCONV1D_WINOGRAD", raising=False)
+    seed = 56_000 + N + C_in + C_out + T + d
+    announce("conv1d_groupnorm_fwd two kernels winograd", (N, C_in, C_out, T, G, d), "seed",
+             seed)
+    p = groupnorm_inputs(N, C_in, C_out, T, seed, with_bias=True)
+    q = to_dev(p)
+    ref = oracle_gn(p, G, d, d)
+
+    def run():
+        o = dc.conv1d_groupnorm_fwd(q["x"], q["W"], q["bias"], q["gamma"], q["beta"], q["eps"],
+                                    G, d, d)
+        torch.cuda.synchronize()
+        return o.cpu().numpy()
+
+    assert dc.dconv1d_groupnorm_method(N, C_in, C_out, T, G, d, d, x=q["x"], W=q["W"]) == \
+        dc.DCONV1D_METHOD_WINOGRAD
+    err_w = maxrel(run(), ref)
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "0")
+    err_d = maxrel(run(), ref)
+    announce(f"   max rel err winograd {err_w:.2e}, three-tap {err_d:.2e}")
+    assert err_w <= TOL_F32, err_w
+    assert err_d <= TOL_F32, err_d
