@@ -121,7 +121,7 @@ def winograd_mfma_flops(N, C, L, d, co_tile=256):
     C = 256 and 512) x (input channels padded to 32) x (output pairs, in tiles of 32), two
     flops per multiply-add."""
     d = min(d, L)
-    pairs = -(-L // (2 * d)) * d
+    pairs = d * (L // (2 * d)) + min(d, L % (2 * d))     # pairs with an output in range
     pairs_run = -(-pairs // 32) * 32
     return 8.0 * N * (-(-C // co_tile) * co_tile) * (-(-C // 32) * 32) * pairs_run
 

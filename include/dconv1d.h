@@ -293,7 +293,9 @@ int dconv1d_timer_read(double* total_ms, int64_t* launches);
  * costs (each kernel takes 64*mb channels per workgroup, mb = 4, 2 or 1, whichever
  * minimises the padded channels divided by the tile's relative rate: 1, 0.96, 0.93 for
  * the Winograd kernel, 1, 0.98, 0.95 for the direct one; c_w = c_d when C is a multiple
- * of 256); else DCONV1D_METHOD_DIRECT. On grids of fewer than two workgroups per compute
+ * of 256), each side scaled, when its grid fills at least one round of workgroups (per CU
+ * as many as the tile's registers allow, times 256 CUs), by ceil(rounds) / rounds; else
+ * DCONV1D_METHOD_DIRECT. On grids of fewer than two workgroups per compute
  * unit both kernels halve their channel tile (down to 64), which keeps the Winograd form
  * the faster one there too. The environment variable DCONV1D_WINOGRAD, read at every call,
  * overrides this: "0" selects the direct form always, "1" the Winograd form for every

@@ -258,10 +258,44 @@ long long wino_pairs(int L, int dil) {
 // N = 1 and 2 (C = 256, L = 4096, d = 128) 64-channel tiles took 21 and 28 us against 44
 // and 44 us with 256-channel tiles (the direct kernel's best: 25 and 37 us).
 int wino_channel_blocks(long long N, int C, int L, int dil) {
-  const long long pair_tiles = (wino_pairs(L, dil) + WINO_PAIRS - 1) / WINO_PAIRS;
+  const long long pair_tiles = wino_pair_tiles(L, dil < L ? dil : L);
   int mb = best_channel_tile(C, kRateWino).mb;
   while (mb > 1 && N * pair_tiles * ((C + 64LL * mb - 1) / (64LL * mb)) < 512) mb /= 2;
   return mb;
+}
+
+// Tile shape of the direct float32 kernel: the channel tile above with 128 time steps when
+// that gives at least two workgroups per CU (512), else with 64; when even that leaves
+// one wave per SIMD, half the channel tile (more, smaller workgroups, each x tile read
+// once more), down to 64 channels.
+ConvTile conv_f32_tile(int L_out, int N, int C_out) {
+  auto wgs = [&](int tt, int cot) {
+    return (long long)N * ((L_out + tt - 1) / tt) * ((C_out + cot - 1) / cot);
+  };
+  for (int mb = best_channel_tile(C_out, kRateDirect).mb;; mb /= 2) {
+    if (wgs(128, 64 * mb) >= 512) return {128, mb};
+    if (wgs(64, 64 * mb) >= 512 || mb == 1) return {64, mb};
+  }
+}
+
+// A grid runs in rounds of (workgroups per CU) x 256 workgroups; a grid that overruns a
+// whole number of rounds leaves most CUs idle in its last one. The factor by which that
+// stretches the grid's time, with the workgroups per CU each tile fits in its registers
+// (Winograd 242, 148, 108 VGPRs at mb = 4, 2, 1: 2, 3, 4 per CU; direct kernel at 128
+// steps 239, 160, 124: 2, 3, 4; at 64 steps 144, 96, 72: 3, 5, 7). L = 1024, d = 97,
+// N = 32, C = 256: 544 Winograd workgroups (two rounds, the second nearly empty) took
+// 131.5 us against the direct kernel's 122.2 us in exactly one round of 512.
+// A grid of less than one round is left at 1: its time is one workgroup's, which the
+// channel-tile costs already compare.
+static double round_factor(long long wgs, int per_cu) {
+  const double rounds = (double)wgs / (256.0 * per_cu);
+  return rounds >= 1.0 ? std::ceil(rounds) / rounds : 1.0;
+}
+
+static int wino_per_cu(int mb) { return mb == 4 ? 2 : mb == 2 ? 3 : 4; }
+static int direct_per_cu(ConvTile t) {
+  if (t.tt == 128) return t.mb == 4 ? 2 : t.mb == 2 ? 3 : 4;
+  return t.mb == 4 ? 3 : t.mb == 2 ? 5 : 7;
 }
 
 // Whether the Winograd form is the faster one. It computes 4 products per output pair
@@ -281,26 +315,23 @@ bool wino_faster(long long N, int C, int L, int dil) {
   if (!wino_supported(L) || dil < 1 || N < 1 || C < 1) return false;
   const ChannelTile w = best_channel_tile(C, kRateWino);
   const ChannelTile f = best_channel_tile(C, kRateDirect);
-  return 3 * wino_pairs(L, dil) * w.cost <= 2LL * L * f.cost;
+  // the grids each form launches, for the round factor
+  const int d = dil < L ? dil : L;
+  const int wmb = wino_channel_blocks(N, C, L, d);
+  const long long wgs_w = N * wino_pair_tiles(L, d) * ((C + 64LL * wmb - 1) / (64LL * wmb));
+  const ConvTile t = conv_f32_tile(L, (int)std::min<long long>(N, 0x7fffffffLL), C);
+  const long long wgs_d = N * ((L + t.tt - 1) / t.tt) * ((C + t.co_tile() - 1) / t.co_tile());
+  return 3.0 * wino_pairs(L, dil) * w.cost * round_factor(wgs_w, wino_per_cu(wmb)) <=
+         2.0 * L * f.cost * round_factor(wgs_d, direct_per_cu(t));
 }
 
-// Tile shape of the direct float32 kernel: the channel tile above with 128 time steps when
-// that gives at least two workgroups per CU (512), else with 64; when even that leaves
-// one wave per SIMD, half the channel tile (more, smaller workgroups, each x tile read
-// once more), down to 64 channels.
-ConvTile conv_f32_tile(int L_out, int N, int C_out) {
-  auto wgs = [&](int tt, int cot) {
-    return (long long)N * ((L_out + tt - 1) / tt) * ((C_out + cot - 1) / cot);
-  };
-  for (int mb = best_channel_tile(C_out, kRateDirect).mb;; mb /= 2) {
-    if (wgs(128, 64 * mb) >= 512) return {128, mb};
-    if (wgs(64, 64 * mb) >= 512 || mb == 1) return {64, mb};
-  }
-}
-
+// Pair tiles to launch. Pair p's first output step 2d*(p/d) + p%d grows with p, so the
+// pairs with an output in range are a prefix, d*floor(L/2d) + min(d, L mod 2d) of them;
+// tiles past it would compute nothing (L = 1024, d = 97: 17 tiles instead of the 19 that
+// cover every super-block). The choice of form still counts every super-block's pairs.
 int wino_pair_tiles(int L, int dil) {
-  const long long blocks = ((long long)L + 2LL * dil - 1) / (2LL * dil);   // super-blocks
-  const long long pairs = blocks * dil;
+  const long long d = dil;
+  const long long pairs = d * (L / (2 * d)) + std::min<long long>(d, L % (2 * d));
   return (int)((pairs + WINO_PAIRS - 1) / WINO_PAIRS);
 }
 

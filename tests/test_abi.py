@@ -162,6 +162,9 @@ def test_last_error_is_cleared_on_success():
     (32, 256, 4096, 1500, dc.DCONV1D_METHOD_DIRECT),    # pairs 3000: 9000 > 8192
     (32, 256, 4096, 3000, dc.DCONV1D_METHOD_DIRECT),
     (512, 16, 7, 2, dc.DCONV1D_METHOD_WINOGRAD),        # pairs 4: 12 <= 14
+    # the Winograd grid overruns one round of 512 workgroups by 32 (17 pair tiles x 32
+    # samples) while the direct grid fills exactly one: the round factor (1.88) decides
+    (32, 256, 1024, 97, dc.DCONV1D_METHOD_DIRECT),
     (512, 16, 5, 2, dc.DCONV1D_METHOD_DIRECT),          # pairs 4: 12 > 10
     # d >= L acts as d = L: every pair's second output lies past the end
     (512, 16, 256, 1000, dc.DCONV1D_METHOD_DIRECT), (512, 16, 1, 7, dc.DCONV1D_METHOD_DIRECT),
