@@ -6,8 +6,8 @@
 
     python -m normalisation_dilated_conv1d_amd.profiling warm KERNEL_TRACE_CSV --kernel NAME
         Average and median duration of one kernel's dispatches in a ``--kernel-trace`` run,
-        leaving out the dispatches that follow bench.py's cache-flush fill kernel (reported
-        separately).
+        leaving out the dispatches that follow one of bench.py's cache-flush kernels (a fill
+        or a reduction over a scratch buffer; reported separately).
 
     python -m normalisation_dilated_conv1d_amd.profiling traffic \\
         --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel conv_f32_kernel \\
@@ -113,16 +113,21 @@ def stats_markdown(path: str, cmd: str) -> str:
     return "Command:\n\n```\n" + cmd + "\n```\n\n" + "\n".join(out) + "\n"
 
 
+# kernels of bench.py's cold-cache passes: a scratch buffer overwritten (torch fill) or
+# summed (torch reduction) before each such step
+FLUSH_KERNELS = ("FillFunctor", "reduce_kernel")
+
+
 def warm_split(trace_csv: str, kernel: str):
     """Durations (us) of the dispatches of `kernel` in a ``--kernel-trace`` CSV, split into
-    warm ones and cold ones (those with a fill kernel since the kernel's previous dispatch:
-    bench.py's cold-cache pass overwrites a scratch buffer before each such step)."""
+    warm ones and cold ones (those with a flush kernel, FLUSH_KERNELS, since the kernel's
+    previous dispatch)."""
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
     warm, cold = [], []
     flushed = False
     for r in rows:
         name = r["Kernel_Name"]
-        if "FillFunctor" in name:
+        if any(f in name for f in FLUSH_KERNELS):
             flushed = True
         elif kernel in name:
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
