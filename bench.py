@@ -377,15 +377,18 @@ def main():
     # workload) does not stay resident in the 256 MB last-level cache between steps, and
     # the caches hold the scratch's dirty lines, written back while the step runs; or it
     # is read ("read": summed), which also evicts x but leaves nothing to write back
-    # Each also returns the conv kernel's mean duration over those steps (the library's
-    # event pair around each launch).
+    # The flushed passes also return the conv kernel's mean duration over their steps (the
+    # library's event pair around each launch; the warm pass runs without it, as the pair
+    # adds a little to each step).
     def per_step_ms(flush):
+        import contextlib
+
         import normalisation_dilated_conv1d_amd as dc
 
         scratch = torch.ones(512 * (1 << 20) // 4, device=dev) if flush else None
         sink = torch.empty((), device=dev)
         times = []
-        with dc.KernelTimer() as kt:
+        with (dc.KernelTimer() if flush else contextlib.nullcontext()) as kt:
             for i in range(args.steps):
                 if flush == "write":
                     scratch.fill_(float(i))
@@ -398,7 +401,7 @@ def main():
                 b_ev.record(stream)
                 times.append((a_ev, b_ev))
             torch.cuda.synchronize()
-            k_ms, k_n = kt.read()
+            k_ms, k_n = kt.read() if flush else (0.0, 0)
         ms = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in times)
         del scratch
         return ms[len(ms) // 2], k_ms / max(k_n, 1)
