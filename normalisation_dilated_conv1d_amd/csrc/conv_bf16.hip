@@ -320,6 +320,9 @@ conv_bf16_kernel(ConvF32Args a) {
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8, wr[(2 * par + s) % RING][mb]), bv[it % BR],
                 acc[mb][nb], 0, 0, 0);
+          // block by block in this order: left free, the scheduler moved each B read
+          // down to just before its MFMAs and waited on it there (1-2% slower)
+          __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
