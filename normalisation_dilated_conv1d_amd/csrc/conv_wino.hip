@@ -29,11 +29,14 @@
 //   K loop     = chunks of 32 input channels (no taps: they are inside the transform),
 //                8 MFMA steps of K = 4 each, 32 MFMAs per step.
 //   B operand  = V_j[32 rows][32 pairs] staged through LDS per chunk by all 256 threads:
-//                each thread loads 4 (row, pair) items' four lattice inputs, applies
+//                each thread loads the four lattice inputs of 4 (row, pair) items: one
+//                row and four consecutive pairs by four 16-byte loads when d is 4, 8, 16
+//                or a multiple of 32, L a multiple of 4 and x 16-byte aligned (about 2%
+//                faster), else 4 rows of one pair by sixteen 4-byte loads. It applies
 //                BN+ReLU (med3(fma(x, scale, shift), 0, cap), cap = 0 outside the input),
-//                forms V0..V3 and writes them with one 16-byte store; double-buffered, one
-//                barrier per chunk, the next chunk staged in the middle of the current
-//                one's MFMAs. A row holds, for pair c, the four V_j at
+//                forms V0..V3 and writes each item's with one 16-byte store;
+//                double-buffered, one barrier per chunk, the next chunk staged in the
+//                middle of the current one's MFMAs. A row holds, for pair c, the four V_j at
 //                64*(c/16) + 4*(c%16) + j, so a lane's B values of one MFMA step (pairs
 //                l%16 and 16 + l%16, all four j) are two 16-byte LDS reads.
 //   A operand  = U_j from the repack of prep_wino_kernel, one 16-byte load per (step,
@@ -103,7 +106,9 @@ __device__ __forceinline__ int wino_tile_start(int pt, int d) {
 // GroupNorm). EPI: EPI_RESIDUAL (the block: + bias + residual) or EPI_GN_STATS (y = conv
 // + bias into out, and per (channel, pair tile) the sum, the tile-centred sum of squares
 // and the count of y for the GroupNorm pass).
-template <int WMB, bool BN, int EPI>
+// VX: the vector staging form (below), for a dilation that is a multiple of 4 and divides
+// 32 or is a multiple of it, L a multiple of 4 and x 16-byte aligned.
+template <int WMB, bool BN, int EPI, bool VX>
 __global__ void __launch_bounds__(NTHREADS, 2)
 conv_wino_kernel(ConvF32Args a) {
   constexpr int CO_TILE = 64 * WMB;
@@ -148,11 +153,15 @@ conv_wino_kernel(ConvF32Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[j][mb][nb][r] = 0.f;
 
-  // Staging geometry of this lane: pair c = l % 32 of the tile, rows 8w + 2i + l/32
-  // (i = 0..3) of each chunk. The four lattice steps of the pair and their caps are the
-  // same for every chunk.
-  const int c = l & 31;
-  const int hrow = l >> 5;
+  // Staging geometry of this lane. Scalar form: pair c = l % 32 of the tile, rows
+  // 8w + 2i + l/32 (i = 0..3) of each chunk, one 4-byte load per lattice step. Vector
+  // form: row 8w + l/8 of each chunk and the four pairs c .. c + 3, c = 4(l % 8); their
+  // steps are consecutive and the first is a multiple of 4, so one 16-byte load per
+  // lattice step brings all four, which lie all inside the input or all outside (0 and L
+  // are multiples of 4 too). The lattice steps and their caps are the same for every
+  // chunk.
+  const int c = VX ? 4 * (l & 7) : (l & 31);
+  const int hrow = VX ? (l >> 3) : (l >> 5);
   const int t0c = regular ? T0 + ((c >> lgD) << (lgD + 1)) + (c & (D - 1))
                           : wino_pair_step(WPAIRS * pt + c, d);
   uint32_t toff[4];                         // byte offsets inside a row
@@ -173,9 +182,21 @@ conv_wino_kernel(ConvF32Args a) {
   }
   const int zpos = 64 * (c >> 4) + 4 * (c & 15);   // LDS position of the pair in a row
 
-  float xr[WRPL][4];
+  float xr[WRPL][4];   // scalar form: row i, lattice step m
+  f32x4 xv[4];         // vector form: lattice step m, pairs c .. c + 3
   float sc[WRPL], sh[WRPL];
   auto load_x = [&](int q) {
+    if constexpr (VX) {
+      const int rl = min(KC * q + 8 * w + hrow, a.C_in - 1);
+      const char* rowp = reinterpret_cast<const char*>(xn + (size_t)rl * L);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) xv[m] = *reinterpret_cast<const f32x4*>(rowp + toff[m]);
+      if (BN) {
+        sc[0] = a.scale[KC * q + 8 * w + hrow];
+        sh[0] = a.shift[KC * q + 8 * w + hrow];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < WRPL; ++i) {
       // a padded input channel loads the last real row: its scale and shift are 0
@@ -198,6 +219,25 @@ conv_wino_kernel(ConvF32Args a) {
   // channel has scale = shift = 0); without, x AND a mask that is zero on a padded tap
   // or a padded input channel
   auto store_z = [&](int q, float* dst) {
+    if constexpr (VX) {
+      const uint32_t rkeep = KC * q + 8 * w + hrow < a.C_in ? 0xffffffffu : 0u;
+      float* drow = dst + (8 * w + hrow) * WPITCH + zpos;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float z[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          z[m] = BN ? __builtin_amdgcn_fmed3f(fmaf(xv[m][u], sc[0], sh[0]), 0.f, cap[m])
+                    : __uint_as_float(__float_as_uint(xv[m][u]) & keep[m] & rkeep);
+        f32x4 v;
+        v[0] = z[0] - z[2];
+        v[1] = z[1] + z[2];
+        v[2] = z[2] - z[1];
+        v[3] = z[1] - z[3];
+        *reinterpret_cast<f32x4*>(drow + 4 * u) = v;
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < WRPL; ++i) {
       float z[4];
@@ -448,15 +488,15 @@ conv_wino_kernel(ConvF32Args a) {
   }
 }
 
-template <bool BN, int EPI>
+template <bool BN, int EPI, bool VX>
 static void launch_wmb(const ConvF32Args& a, int wmb, dim3 grid, dim3 block,
                        hipStream_t stream) {
   if (wmb == 4)
-    hipLaunchKernelGGL((conv_wino_kernel<4, BN, EPI>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((conv_wino_kernel<4, BN, EPI, VX>), grid, block, 0, stream, a);
   else if (wmb == 2)
-    hipLaunchKernelGGL((conv_wino_kernel<2, BN, EPI>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((conv_wino_kernel<2, BN, EPI, VX>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((conv_wino_kernel<1, BN, EPI>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((conv_wino_kernel<1, BN, EPI, VX>), grid, block, 0, stream, a);
 }
 
 hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, int epilogue, hipStream_t stream) {
@@ -474,10 +514,18 @@ hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, int epilogue, hipStre
       a.NCB * 16 < a.n_ct * 64 * wmb || a.Q * KC < a.C_in)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(NTHREADS);
-  if (block_ok)
-    launch_wmb<true, EPI_RESIDUAL>(a, wmb, grid, block, stream);
+  // the vector staging form: d a multiple of 4 that divides 32 or is a multiple of 32
+  const int d = a.dil;
+  const bool vx = (d % 32 == 0 || (d >= 4 && 32 % d == 0)) && a.L_in % 4 == 0 &&
+                  (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+  if (block_ok && vx)
+    launch_wmb<true, EPI_RESIDUAL, true>(a, wmb, grid, block, stream);
+  else if (block_ok)
+    launch_wmb<true, EPI_RESIDUAL, false>(a, wmb, grid, block, stream);
+  else if (vx)
+    launch_wmb<false, EPI_GN_STATS, true>(a, wmb, grid, block, stream);
   else
-    launch_wmb<false, EPI_GN_STATS>(a, wmb, grid, block, stream);
+    launch_wmb<false, EPI_GN_STATS, false>(a, wmb, grid, block, stream);
   return hipGetLastError();
 }
 

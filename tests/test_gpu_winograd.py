@@ -255,3 +255,68 @@ def test_groupnorm_two_kernel_winograd(N, C_in, C_out, T, G, d, monkeypatch):
     announce(f"   max rel err winograd {err_w:.2e}, three-tap {err_d:.2e}")
     assert err_w <= TOL_F32, err_w
     assert err_d <= TOL_F32, err_d
+
+
+STAGING_CASES = [
+    # (N, C, L, d): d a multiple of 4 that divides 32 or is a multiple of 32, L % 4 == 0
+    (2, 64, 1024, 128),
+    (2, 48, 1000, 8),
+    (3, 288, 4100, 4),       # two channel tiles, ragged last pair tile
+    (2, 40, 2048, 96),       # C_in not a multiple of 32: padded rows in the last chunk
+]
+
+
+def _shifted(t):
+    """A copy of t one float into a buffer: 4-byte aligned, never 16-byte aligned."""
+    buf = torch.empty(t.numel() + 4, device="cuda", dtype=t.dtype)
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+@pytest.mark.parametrize("N,C,L,d", STAGING_CASES)
+def test_winograd_staging_forms_agree(N, C, L, d, monkeypatch):
+    """With x 16-byte aligned the Winograd kernel stages four pairs per 16-byte load; with
+    x one float into a buffer, one pair per 4-byte load. Both stage the same values, so
+    the outputs agree bit for bit (the residual, the same x, then takes the per-element
+    epilogue, whose sums run in the same order), and both match the oracle."""
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
+    seed = 57_000 + N + C + L + d
+    announce("prenorm_dconv1d_fwd winograd staging forms", (N, C, L, d), "seed", seed)
+    p = prenorm_inputs(N, C, L, seed)
+    aligned = run_block(p, d).cpu()
+    q = to_dev(p)
+    shifted = dc.prenorm_dconv1d_fwd(_shifted(q["x"]), q["running_mean"], q["running_var"],
+                                     q["gamma"], q["beta"], q["eps"], q["W"], q["b"], d)
+    torch.cuda.synchronize()
+    assert torch.equal(shifted.cpu(), aligned)
+    err = maxrel(aligned.numpy(), oracle_block(p, d))
+    announce(f"   max rel err {err:.2e}")
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("N,C_in,C_out,T,G,d", [(2, 32, 64, 2048, 8, 4),
+                                                (2, 32, 64, 2500, 4, 64)])
+def test_groupnorm_two_kernel_staging_forms_agree(N, C_in, C_out, T, G, d, monkeypatch):
+    """The same two staging forms in the two-kernel GroupNorm path's Winograd conv."""
+    monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
+    seed = 57_500 + N + C_in + C_out + T + d
+    announce("conv1d_groupnorm_fwd two kernels staging forms", (N, C_in, C_out, T, G, d),
+             "seed", seed)
+    p = groupnorm_inputs(N, C_in, C_out, T, seed, with_bias=True)
+    q = to_dev(p)
+    assert dc.dconv1d_groupnorm_method(N, C_in, C_out, T, G, d, d, x=q["x"], W=q["W"]) == \
+        dc.DCONV1D_METHOD_WINOGRAD
+
+    def run(x):
+        o = dc.conv1d_groupnorm_fwd(x, q["W"], q["bias"], q["gamma"], q["beta"], q["eps"],
+                                    G, d, d)
+        torch.cuda.synchronize()
+        return o.cpu()
+
+    aligned = run(q["x"])
+    assert torch.equal(run(_shifted(q["x"])), aligned)
+    err = maxrel(aligned.numpy(), oracle_gn(p, G, d, d))
+    announce(f"   max rel err {err:.2e}")
+    assert err <= TOL_F32, err
