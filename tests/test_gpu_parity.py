@@ -387,6 +387,30 @@ def test_block_bf16_deterministic():
     assert all(torch.equal(outs[0], r) for r in outs[1:])
 
 
+@pytest.mark.parametrize("N,C,L,d", [(2, 512, 2048, 128), (2, 64, 1024, 8)])
+def test_block_bf16_x_load_forms_agree(N, C, L, d):
+    """The bf16 kernel's x load forms stage the same values: x 4-byte aligned (2 steps per
+    buffer->LDS load) and 2-byte aligned (1 step per load into registers) give the same
+    bits, and so do the 16-byte and per-element epilogues. x sits 2 or 1 elements into a
+    buffer; the residual, the same x, then takes the per-element epilogue."""
+    announce("prenorm_dconv1d_fwd_bf16 x load forms", (N, C, L, d))
+    q = to_dev(prenorm_inputs(N, C, L, 45, bf16=True))
+
+    def run(x):
+        o = dc.prenorm_dconv1d_fwd_bf16(x, q["running_mean"], q["running_var"], q["gamma"],
+                                        q["beta"], q["eps"], q["W"], q["b"], d)
+        torch.cuda.synchronize()
+        return o.cpu()
+
+    ref = run(q["x"])
+    for shift in (2, 1):
+        buf = torch.empty(q["x"].numel() + 8, device="cuda", dtype=q["x"].dtype)
+        x = buf[shift:shift + q["x"].numel()].view(q["x"].shape)
+        x.copy_(q["x"])
+        assert x.data_ptr() % 16 != 0
+        assert torch.equal(run(x), ref), shift
+
+
 # ----------------------------------------------------------------- full benchmark workloads
 
 def test_workload0_tiny():
