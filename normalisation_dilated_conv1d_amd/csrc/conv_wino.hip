@@ -30,9 +30,10 @@
 //                8 MFMA steps of K = 4 each, 32 MFMAs per step.
 //   B operand  = V_j[32 rows][32 pairs] staged through LDS per chunk by all 256 threads:
 //                each thread loads the four lattice inputs of 4 (row, pair) items: one
-//                row and four consecutive pairs by four 16-byte loads when d is 4, 8, 16
-//                or a multiple of 32, L a multiple of 4 and x 16-byte aligned (about 2%
-//                faster), else 4 rows of one pair by sixteen 4-byte loads. It applies
+//                row and four consecutive pairs by four 16-byte loads when L is a
+//                multiple of 4 and x 16-byte aligned (one load per lattice step when d is
+//                4, 8, 16 or a multiple of 32; the 16 steps around the pairs when d is 1
+//                or 2), else 4 rows of one pair by sixteen 4-byte loads. It applies
 //                BN+ReLU (med3(fma(x, scale, shift), 0, cap), cap = 0 outside the input),
 //                forms V0..V3 and writes each item's with one 16-byte store;
 //                double-buffered, one barrier per chunk, the next chunk staged in the
@@ -84,6 +85,11 @@ __device__ __forceinline__ float quarterwave_sum(float v) {
   return v;
 }
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 // first output step of pair p
 __device__ __forceinline__ int wino_pair_step(int p, int d) {
   const int b = p / d;
@@ -106,9 +112,11 @@ __device__ __forceinline__ int wino_tile_start(int pt, int d) {
 // GroupNorm). EPI: EPI_RESIDUAL (the block: + bias + residual) or EPI_GN_STATS (y = conv
 // + bias into out, and per (channel, pair tile) the sum, the tile-centred sum of squares
 // and the count of y for the GroupNorm pass).
-// VX: the vector staging form (below), for a dilation that is a multiple of 4 and divides
-// 32 or is a multiple of it, L a multiple of 4 and x 16-byte aligned.
-template <int WMB, bool BN, int EPI, bool VX>
+// SX: the staging form (below): SX_SCALAR for any shape; SX_LATTICE for d = 4, 8, 16 or
+// a multiple of 32, SX_WINDOW1 for d = 1 and SX_WINDOW2 for d = 2, each with L a multiple
+// of 4 and x 16-byte aligned.
+enum { SX_SCALAR = 0, SX_LATTICE = 1, SX_WINDOW1 = 2, SX_WINDOW2 = 3 };
+template <int WMB, bool BN, int EPI, int SX>
 __global__ void __launch_bounds__(NTHREADS, 2)
 conv_wino_kernel(ConvF32Args a) {
   constexpr int CO_TILE = 64 * WMB;
@@ -154,14 +162,15 @@ conv_wino_kernel(ConvF32Args a) {
         for (int r = 0; r < 4; ++r) acc[j][mb][nb][r] = 0.f;
 
   // Staging geometry of this lane. Scalar form: pair c = l % 32 of the tile, rows
-  // 8w + 2i + l/32 (i = 0..3) of each chunk, one 4-byte load per lattice step. Vector
-  // form: row 8w + l/8 of each chunk and the four pairs c .. c + 3, c = 4(l % 8); their
-  // steps are consecutive and the first is a multiple of 4, so one 16-byte load per
-  // lattice step brings all four, which lie all inside the input or all outside (0 and L
-  // are multiples of 4 too). The lattice steps and their caps are the same for every
-  // chunk.
-  const int c = VX ? 4 * (l & 7) : (l & 31);
-  const int hrow = VX ? (l >> 3) : (l >> 5);
+  // 8w + 2i + l/32 (i = 0..3) of each chunk, one 4-byte load per lattice step. The other
+  // two: row 8w + l/8 of each chunk and the four pairs c .. c + 3, c = 4(l % 8), with
+  // 16-byte loads of 4 steps from a multiple of 4, which lie all inside the input or all
+  // outside (0 and L are multiples of 4 too). Lattice form: the four pairs' steps are
+  // consecutive, so one load per lattice step brings all four. Window form (d = 1 or 2):
+  // the four pairs' 16 lattice inputs lie in the 16 steps from t0c - 4 on, four loads.
+  // The loaded steps and their caps are the same for every chunk.
+  const int c = SX != SX_SCALAR ? 4 * (l & 7) : (l & 31);
+  const int hrow = SX != SX_SCALAR ? (l >> 3) : (l >> 5);
   const int t0c = regular ? T0 + ((c >> lgD) << (lgD + 1)) + (c & (D - 1))
                           : wino_pair_step(WPAIRS * pt + c, d);
   uint32_t toff[4];                         // byte offsets inside a row
@@ -169,7 +178,8 @@ conv_wino_kernel(ConvF32Args a) {
   uint32_t keep[4];                         // no BN: all ones inside the input, 0 on padding
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int t = t0c + (m - 1) * d;      // |t| < 2^30: L, d < 2^28
+    // lattice step m, or window group m; |t| < 2^30: L, d < 2^28
+    const int t = SX >= SX_WINDOW1 ? t0c - 4 + 4 * m : t0c + (m - 1) * d;
     const bool in = t >= 0 && t < L;
     // an outside step loads any in-range step: its cap makes it zero
     toff[m] = 4u * (uint32_t)(in ? t : 0);
@@ -183,10 +193,10 @@ conv_wino_kernel(ConvF32Args a) {
   const int zpos = 64 * (c >> 4) + 4 * (c & 15);   // LDS position of the pair in a row
 
   float xr[WRPL][4];   // scalar form: row i, lattice step m
-  f32x4 xv[4];         // vector form: lattice step m, pairs c .. c + 3
+  f32x4 xv[4];         // lattice form: step m of pairs c .. c + 3; window form: group m
   float sc[WRPL], sh[WRPL];
   auto load_x = [&](int q) {
-    if constexpr (VX) {
+    if constexpr (SX != SX_SCALAR) {
       const int rl = min(KC * q + 8 * w + hrow, a.C_in - 1);
       const char* rowp = reinterpret_cast<const char*>(xn + (size_t)rl * L);
 #pragma unroll
@@ -219,22 +229,37 @@ conv_wino_kernel(ConvF32Args a) {
   // channel has scale = shift = 0); without, x AND a mask that is zero on a padded tap
   // or a padded input channel
   auto store_z = [&](int q, float* dst) {
-    if constexpr (VX) {
+    if constexpr (SX != SX_SCALAR) {
       const uint32_t rkeep = KC * q + 8 * w + hrow < a.C_in ? 0xffffffffu : 0u;
       float* drow = dst + (8 * w + hrow) * WPITCH + zpos;
+      // the four pairs, with the loaded value (group g, element e) of lattice step m of
+      // pair u given by pos(u, m) = 4g + e
+      auto stage = [&](auto pos) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float z[4];
+        for (int u = 0; u < 4; ++u) {
+          float z[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          z[m] = BN ? __builtin_amdgcn_fmed3f(fmaf(xv[m][u], sc[0], sh[0]), 0.f, cap[m])
-                    : __uint_as_float(__float_as_uint(xv[m][u]) & keep[m] & rkeep);
-        f32x4 v;
-        v[0] = z[0] - z[2];
-        v[1] = z[1] + z[2];
-        v[2] = z[2] - z[1];
-        v[3] = z[1] - z[3];
-        *reinterpret_cast<f32x4*>(drow + 4 * u) = v;
+          for (int m = 0; m < 4; ++m) {
+            const int g = pos(u, m) >> 2, e = pos(u, m) & 3;
+            z[m] = BN ? __builtin_amdgcn_fmed3f(fmaf(xv[g][e], sc[0], sh[0]), 0.f, cap[g])
+                      : __uint_as_float(__float_as_uint(xv[g][e]) & keep[g] & rkeep);
+          }
+          f32x4 v;
+          v[0] = z[0] - z[2];
+          v[1] = z[1] + z[2];
+          v[2] = z[2] - z[1];
+          v[3] = z[1] - z[3];
+          *reinterpret_cast<f32x4*>(drow + 4 * u) = v;
+        }
+      };
+      if constexpr (SX == SX_LATTICE) {
+        stage([](int u, int m) { return 4 * m + u; });
+      } else if constexpr (SX == SX_WINDOW1) {
+        // pair u is (t0c + 2u, t0c + 2u + 1): step m at t0c + 2u + m - 1
+        stage([](int u, int m) { return 2 * u + m + 3; });
+      } else {
+        // d = 2: pair u is (t0c + 4(u/2) + u%2, + 2): step m at that + 2(m - 1)
+        stage([](int u, int m) { return 4 * (u >> 1) + (u & 1) + 2 * m + 2; });
       }
       return;
     }
@@ -488,15 +513,15 @@ conv_wino_kernel(ConvF32Args a) {
   }
 }
 
-template <bool BN, int EPI, bool VX>
+template <bool BN, int EPI, int SX>
 static void launch_wmb(const ConvF32Args& a, int wmb, dim3 grid, dim3 block,
                        hipStream_t stream) {
   if (wmb == 4)
-    hipLaunchKernelGGL((conv_wino_kernel<4, BN, EPI, VX>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((conv_wino_kernel<4, BN, EPI, SX>), grid, block, 0, stream, a);
   else if (wmb == 2)
-    hipLaunchKernelGGL((conv_wino_kernel<2, BN, EPI, VX>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((conv_wino_kernel<2, BN, EPI, SX>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((conv_wino_kernel<1, BN, EPI, VX>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((conv_wino_kernel<1, BN, EPI, SX>), grid, block, 0, stream, a);
 }
 
 hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, int epilogue, hipStream_t stream) {
@@ -514,18 +539,31 @@ hipError_t launch_conv_wino(const ConvF32Args& a, int wmb, int epilogue, hipStre
       a.NCB * 16 < a.n_ct * 64 * wmb || a.Q * KC < a.C_in)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(NTHREADS);
-  // the vector staging form: d a multiple of 4 that divides 32 or is a multiple of 32
+  // the staging form: 16-byte loads need L a multiple of 4 and x 16-byte aligned
   const int d = a.dil;
-  const bool vx = (d % 32 == 0 || (d >= 4 && 32 % d == 0)) && a.L_in % 4 == 0 &&
-                  (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
-  if (block_ok && vx)
-    launch_wmb<true, EPI_RESIDUAL, true>(a, wmb, grid, block, stream);
-  else if (block_ok)
-    launch_wmb<true, EPI_RESIDUAL, false>(a, wmb, grid, block, stream);
-  else if (vx)
-    launch_wmb<false, EPI_GN_STATS, true>(a, wmb, grid, block, stream);
-  else
-    launch_wmb<false, EPI_GN_STATS, false>(a, wmb, grid, block, stream);
+  const bool v16 = a.L_in % 4 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+  const int sx = !v16 ? SX_SCALAR
+                 : d % 32 == 0 || (d >= 4 && 32 % d == 0) ? SX_LATTICE
+                 : d == 1 ? SX_WINDOW1 : d == 2 ? SX_WINDOW2 : SX_SCALAR;
+  if (block_ok) {
+    if (sx == SX_LATTICE)
+      launch_wmb<true, EPI_RESIDUAL, SX_LATTICE>(a, wmb, grid, block, stream);
+    else if (sx == SX_WINDOW1)
+      launch_wmb<true, EPI_RESIDUAL, SX_WINDOW1>(a, wmb, grid, block, stream);
+    else if (sx == SX_WINDOW2)
+      launch_wmb<true, EPI_RESIDUAL, SX_WINDOW2>(a, wmb, grid, block, stream);
+    else
+      launch_wmb<true, EPI_RESIDUAL, SX_SCALAR>(a, wmb, grid, block, stream);
+  } else {
+    if (sx == SX_LATTICE)
+      launch_wmb<false, EPI_GN_STATS, SX_LATTICE>(a, wmb, grid, block, stream);
+    else if (sx == SX_WINDOW1)
+      launch_wmb<false, EPI_GN_STATS, SX_WINDOW1>(a, wmb, grid, block, stream);
+    else if (sx == SX_WINDOW2)
+      launch_wmb<false, EPI_GN_STATS, SX_WINDOW2>(a, wmb, grid, block, stream);
+    else
+      launch_wmb<false, EPI_GN_STATS, SX_SCALAR>(a, wmb, grid, block, stream);
+  }
   return hipGetLastError();
 }
 

@@ -258,11 +258,15 @@ def test_groupnorm_two_kernel_winograd(N, C_in, C_out, T, G, d, monkeypatch):
 
 
 STAGING_CASES = [
-    # (N, C, L, d): d a multiple of 4 that divides 32 or is a multiple of 32, L % 4 == 0
+    # (N, C, L, d): d a multiple of 4 that divides 32 or is a multiple of 32, L % 4 == 0:
+    # one 16-byte load per lattice step of four pairs
     (2, 64, 1024, 128),
     (2, 48, 1000, 8),
     (3, 288, 4100, 4),       # two channel tiles, ragged last pair tile
     (2, 40, 2048, 96),       # C_in not a multiple of 32: padded rows in the last chunk
+    # d = 1 or 2 (L a multiple of 4): 16-byte loads of the 16 steps around four pairs
+    (2, 64, 1024, 1),
+    (3, 96, 2052, 2),        # ragged last pair tile
 ]
 
 
@@ -277,8 +281,8 @@ def _shifted(t):
 
 @pytest.mark.parametrize("N,C,L,d", STAGING_CASES)
 def test_winograd_staging_forms_agree(N, C, L, d, monkeypatch):
-    """With x 16-byte aligned the Winograd kernel stages four pairs per 16-byte load; with
-    x one float into a buffer, one pair per 4-byte load. Both stage the same values, so
+    """With x 16-byte aligned the Winograd kernel stages four pairs with 16-byte loads;
+    with x one float into a buffer, one pair per 4-byte load. Both stage the same values, so
     the outputs agree bit for bit (the residual, the same x, then takes the per-element
     epilogue, whose sums run in the same order), and both match the oracle."""
     monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
@@ -297,7 +301,9 @@ def test_winograd_staging_forms_agree(N, C, L, d, monkeypatch):
 
 
 @pytest.mark.parametrize("N,C_in,C_out,T,G,d", [(2, 32, 64, 2048, 8, 4),
-                                                (2, 32, 64, 2500, 4, 64)])
+                                                (2, 32, 64, 2500, 4, 64),
+                                                (2, 32, 64, 2048, 8, 1),
+                                                (1, 48, 96, 3000, 12, 2)])
 def test_groupnorm_two_kernel_staging_forms_agree(N, C_in, C_out, T, G, d, monkeypatch):
     """The same two staging forms in the two-kernel GroupNorm path's Winograd conv."""
     monkeypatch.setenv("DCONV1D_WINOGRAD", "1")
